@@ -1,0 +1,284 @@
+"""Plain CPU oracle for the low-bit-weight linear layer.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path may import or call this
+module: only the tests, the package smoke check and the benchmark's CPU-baseline
+leg use it. It shares no code with the GPU library.
+
+What it computes, and where the pages say so
+---------------------------------------------
+* Weight definition (page "Cómo Bonsai Ternary 4B revoluciona la difusión
+  texto-imagen", section "Representación y almacenamiento de los pesos
+  ternarios"): each weight is ``w = scale_g * t`` with ``t`` in {-1, 0, +1} and one
+  FP16 scale shared by every group of 128 weights; the CUDA deployment stores
+  ``t`` with 2 bits per ternary value (INT2).
+* Binary variant (page "Bonsai Image 4B 1-bit untuk pembuatan gambar di
+  perangkat lokal", section on the two variants; page "Introducing 1-bit and
+  Ternary Bonsai Image 4B", section "量化数学"): ``t`` in {-1, +1}, same FP16 group
+  scale, 1 bit per weight plus 16/128 bits of scale = 1.125 bits per weight.
+* The layer computes ``Y = X W^T (+ bias)``. The oracle dequantises W exactly and
+  forms the matrix product in float64, which for these operands is the exact real
+  result up to a relative error of about K * 2^-53 (every product
+  ``x * s * t`` is exact in float64: 8 or 11 significand bits times 11 bits).
+
+Readings where the pages are silent (each is listed in the design notes):
+* INT2 code of a ternary value: ``c = t + 1`` in {0, 1, 2}; the value 3 is invalid.
+* Bit order: a packed row is a sequence of little-endian 32-bit words. Ternary:
+  word ``u`` holds k = 16u .. 16u+15; the code of k = 16u + 2i + h (i in 0..7,
+  h in {0, 1}) sits at bits [16h + 2i, 16h + 2i + 1]. Even k fill the low half
+  word, odd k the high half word. Binary: word ``u`` holds k = 32u .. 32u+31; the
+  bit of k = 32u + 2i + h (i in 0..15) sits at bit 16h + i; bit 1 means +1.
+* Groups run along K inside one output row; K must be a multiple of 128.
+* The bias, when present, is added once in the output row sum.
+* Output cast: round to nearest, ties to even.
+
+Parity: the GPU result must satisfy, per element,
+``|Y - A| <= 1e-3 * sum_k |x_k w_k| + 1e-5`` (the stated tolerance; the bias
+magnitude joins the sum as one more term), plus half an output ulp when the
+output type is fp16 or bf16, and non-finite values must match in place.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Tuple
+
+import numpy as np
+
+GROUP = 128
+
+# ---------------------------------------------------------------------------
+# 16-bit float formats: decode exactly, encode with round-to-nearest-even
+# ---------------------------------------------------------------------------
+
+# (significand bits incl. the implicit one, minimum normal exponent, maximum finite)
+_FORMATS = {
+    "f16": (11, -14, 65504.0),
+    "bf16": (8, -126, float(np.float32(3.3895313892515355e38))),
+}
+
+
+def decode(bits: np.ndarray, dtype: str) -> np.ndarray:
+    """16-bit pattern -> float64 (exact). ``dtype`` 'f16', 'bf16' or 'f32' (32-bit bits)."""
+    bits = np.asarray(bits)
+    if dtype == "f16":
+        return bits.astype(np.uint16).view(np.float16).astype(np.float64)
+    if dtype == "bf16":
+        return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    if dtype == "f32":
+        return bits.astype(np.uint32).view(np.float32).astype(np.float64)
+    raise ValueError(dtype)
+
+
+def round_to(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float64 values to the nearest value of ``dtype`` (ties to even).
+
+    Returns float64 values that are exactly representable in ``dtype``; overflow
+    past the largest finite value (by half an ulp or more) gives +-inf.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if dtype == "f32":
+        return x.astype(np.float32).astype(np.float64)
+    p, emin, fmax = _FORMATS[dtype]
+    out = np.array(x, dtype=np.float64, copy=True)
+    fin = np.isfinite(x) & (x != 0)
+    v = x[fin]
+    _, e = np.frexp(v)                       # v = m * 2^e, 0.5 <= |m| < 1
+    # exponent of the leading bit is e-1; quantum = 2^(e-1-(p-1)) but never below
+    # the subnormal spacing 2^(emin-(p-1))
+    q_exp = np.maximum(e - p, emin - (p - 1))
+    q = np.ldexp(1.0, q_exp)
+    r = np.rint(v / q) * q                   # np.rint: ties to even; v/q exact (power of 2)
+    # overflow: anything that rounded above the largest finite value. A value at
+    # fmax + ulp/2 is a tie whose even neighbour is the next power of two, so it
+    # also lands here and becomes inf, as round-to-nearest-even requires.
+    big = np.abs(r) > fmax
+    r[big] = np.copysign(np.inf, r[big])
+    out[fin] = r
+    return out
+
+
+def encode(x: np.ndarray, dtype: str) -> np.ndarray:
+    """float64 -> bit pattern of ``dtype`` after round-to-nearest-even."""
+    r = round_to(x, dtype)
+    if dtype == "f16":
+        return r.astype(np.float16).view(np.uint16)
+    if dtype == "bf16":
+        f = r.astype(np.float32)             # exact: r is a bf16 value
+        u = f.view(np.uint32)
+        out = (u >> 16).astype(np.uint16)
+        nan = np.isnan(r)
+        out[nan] = 0x7FC0
+        return out
+    if dtype == "f32":
+        return r.astype(np.float32).view(np.uint32)
+    raise ValueError(dtype)
+
+
+def ulp(v: np.ndarray, dtype: str) -> np.ndarray:
+    """Spacing of ``dtype`` values at magnitude |v| (subnormal spacing near 0)."""
+    v = np.abs(np.asarray(v, dtype=np.float64))
+    if dtype == "f32":
+        p, emin = 24, -126
+    else:
+        p, emin, _ = _FORMATS[dtype]
+    with np.errstate(divide="ignore"):
+        _, e = np.frexp(np.where(v > 0, v, 1.0))
+    e = np.where(v > 0, e, emin + 1)
+    return np.ldexp(1.0, np.maximum(e - p, emin - (p - 1)))
+
+
+# ---------------------------------------------------------------------------
+# Packing (the INT2 / 1-bit storage the pages describe, in this library's layout)
+# ---------------------------------------------------------------------------
+
+def pack_ternary(t: np.ndarray) -> np.ndarray:
+    """int8 codes [N, K] in {-1,0,+1} -> uint8 [N, K/4] (2 bits per weight)."""
+    t = np.asarray(t)
+    N, K = t.shape
+    if K % 16:
+        raise ValueError("ternary packing needs K % 16 == 0")
+    if not np.isin(t, (-1, 0, 1)).all():
+        raise ValueError("ternary codes must lie in {-1, 0, +1}")
+    c = (t.astype(np.int64) + 1).astype(np.uint32)          # offset code 0, 1, 2
+    words = np.zeros((N, K // 16), dtype=np.uint32)
+    for j in range(16):                                      # position inside the word
+        i, h = divmod(j, 2)
+        words |= c[:, j::16] << np.uint32(16 * h + 2 * i)
+    return words.astype("<u4").view(np.uint8).reshape(N, K // 4)
+
+
+def pack_binary(t: np.ndarray) -> np.ndarray:
+    """int8 codes [N, K] in {-1,+1} -> uint8 [N, K/8] (1 bit per weight, 1 = +1)."""
+    t = np.asarray(t)
+    N, K = t.shape
+    if K % 32:
+        raise ValueError("binary packing needs K % 32 == 0")
+    if not np.isin(t, (-1, 1)).all():
+        raise ValueError("binary codes must lie in {-1, +1}")
+    b = (t == 1).astype(np.uint32)
+    words = np.zeros((N, K // 32), dtype=np.uint32)
+    for j in range(32):
+        i, h = divmod(j, 2)
+        words |= b[:, j::32] << np.uint32(16 * h + i)
+    return words.astype("<u4").view(np.uint8).reshape(N, K // 8)
+
+
+def unpack_ternary(packed: np.ndarray, K: int) -> Tuple[np.ndarray, int]:
+    """uint8 [N, K/4] -> (int8 codes [N, K], number of invalid 2-bit fields).
+
+    An invalid field (value 3) decodes to 0 and is counted."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    N = packed.shape[0]
+    words = packed.reshape(N, K // 4).view("<u4").astype(np.uint32)
+    t = np.zeros((N, K), dtype=np.int8)
+    invalid = 0
+    for j in range(16):
+        i, h = divmod(j, 2)
+        c = (words >> np.uint32(16 * h + 2 * i)) & np.uint32(3)
+        invalid += int((c == 3).sum())
+        t[:, j::16] = np.where(c == 3, 0, c.astype(np.int64) - 1).astype(np.int8)
+    return t, invalid
+
+
+def unpack_binary(packed: np.ndarray, K: int) -> np.ndarray:
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    N = packed.shape[0]
+    words = packed.reshape(N, K // 8).view("<u4").astype(np.uint32)
+    t = np.zeros((N, K), dtype=np.int8)
+    for j in range(32):
+        i, h = divmod(j, 2)
+        b = (words >> np.uint32(16 * h + i)) & np.uint32(1)
+        t[:, j::32] = (2 * b.astype(np.int64) - 1).astype(np.int8)
+    return t
+
+
+def packed_bytes(fmt: str, N: int, K: int) -> int:
+    return N * K // (4 if fmt == "ternary" else 8)
+
+
+def scale_bytes(N: int, K: int, group: int = GROUP) -> int:
+    return 2 * N * (K // group)
+
+
+# ---------------------------------------------------------------------------
+# Dequantisation and the layer
+# ---------------------------------------------------------------------------
+
+def dequantize(t: np.ndarray, scales: np.ndarray, group: int = GROUP) -> np.ndarray:
+    """W[n, k] = float(scale[n, k // group]) * t[n, k], exactly, in float64."""
+    t = np.asarray(t)
+    N, K = t.shape
+    if K % group:
+        raise ValueError("K must be a multiple of the group size")
+    s = np.asarray(scales, dtype=np.float16).astype(np.float64)
+    if s.shape != (N, K // group):
+        raise ValueError("scales must have shape [N, K/group]")
+    return np.repeat(s, group, axis=1) * t.astype(np.float64)
+
+
+def linear(x_bits: np.ndarray, x_dtype: str, t: np.ndarray, scales: np.ndarray,
+           bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """A[m, n] = sum_k x[m, k] * w[n, k] (+ bias[n]) in float64 (near exact)."""
+    X = decode(x_bits, x_dtype)
+    W = dequantize(t, scales)
+    A = X @ W.T
+    if bias is not None:
+        A = A + np.asarray(bias, dtype=np.float16).astype(np.float64)[None, :]
+    return A
+
+
+def magnitude(x_bits: np.ndarray, x_dtype: str, t: np.ndarray, scales: np.ndarray,
+              bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """sum_k |x[m, k] * w[n, k]| (+ |bias[n]|): the scale of the tolerance."""
+    X = np.abs(decode(x_bits, x_dtype))
+    W = np.abs(dequantize(t, scales))
+    Mg = X @ W.T
+    if bias is not None:
+        Mg = Mg + np.abs(np.asarray(bias, dtype=np.float16).astype(np.float64))[None, :]
+    return Mg
+
+
+def gelu(a: np.ndarray) -> np.ndarray:
+    """Exact-erf GELU, x * Phi(x) = 0.5 x (1 + erf(x / sqrt 2)), in float64."""
+    from scipy.special import erf
+    a = np.asarray(a, dtype=np.float64)
+    return 0.5 * a * (1.0 + erf(a / math.sqrt(2.0)))
+
+
+# ---------------------------------------------------------------------------
+# Tolerance
+# ---------------------------------------------------------------------------
+
+REL_TOL = 1e-3
+ABS_TOL = 1e-5
+
+
+def bound(A: np.ndarray, Mg: np.ndarray, y_dtype: str, Y: Optional[np.ndarray] = None) -> np.ndarray:
+    """Largest admissible |Y - A| per element.
+
+    1e-3 * Mg + 1e-5, plus half an output ulp (taken at the larger of |A| and |Y|)
+    when the output is fp16 or bf16, because the final cast may move the value by
+    that much on its own."""
+    b = REL_TOL * Mg + ABS_TOL
+    if y_dtype in ("f16", "bf16"):
+        ref = np.abs(A) if Y is None else np.maximum(np.abs(A), np.abs(Y))
+        b = b + 0.5 * ulp(ref, y_dtype)
+    return b
+
+
+def check(Y: np.ndarray, A: np.ndarray, Mg: np.ndarray, y_dtype: str):
+    """Return (ok, worst ratio |Y-A|/bound, number of failing elements).
+
+    ``Y`` is float64 (decoded output). Non-finite entries must match in place
+    (NaN where A is NaN, equal infinities)."""
+    Y = np.asarray(Y, dtype=np.float64)
+    A = np.asarray(A, dtype=np.float64)
+    fin = np.isfinite(A)
+    bad_nf = int((~fin & ~((np.isnan(A) & np.isnan(Y)) | (A == Y))).sum())
+    d = np.abs(Y[fin] - A[fin])
+    b = bound(A[fin], Mg[fin], y_dtype, Y[fin])
+    with np.errstate(invalid="ignore"):
+        ratio = np.where(b > 0, d / b, np.where(d > 0, np.inf, 0.0))
+    ratio = np.where(np.isnan(ratio), np.inf, ratio)
+    nfail = int((ratio > 1.0).sum()) + bad_nf
+    worst = float(ratio.max()) if ratio.size else 0.0
+    return nfail == 0, worst, nfail

@@ -1,0 +1,341 @@
+"""Pins for the CPU oracle: values, closed forms and invariants that come from the
+pages and from mathematics, not from the oracle itself. CPU only."""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+
+
+def _golden(golden_dir, name):
+    with open(os.path.join(golden_dir, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- packing ---
+
+def test_ternary_pack_hand_literal(golden_dir):
+    g = _golden(golden_dir, "ternary_pack_word.json")
+    t = np.array([g["t"]], dtype=np.int8)
+    p = oracle.pack_ternary(t)
+    assert p.tobytes().hex() == g["packed_hex"]
+
+
+def test_binary_pack_hand_literal(golden_dir):
+    g = _golden(golden_dir, "binary_pack_word.json")
+    t = -np.ones((1, g["K"]), dtype=np.int8)
+    t[0, g["plus_positions"]] = 1
+    assert oracle.pack_binary(t).tobytes().hex() == g["packed_hex"]
+
+
+# which k (inside one 16-code word) each 2-bit field of each byte carries
+_TERNARY_BYTE_K = {0: [0, 2, 4, 6], 1: [8, 10, 12, 14], 2: [1, 3, 5, 7], 3: [9, 11, 13, 15]}
+
+
+@pytest.mark.parametrize("byte", [0, 1, 2, 3])
+def test_ternary_every_valid_byte(byte):
+    """All 3^4 = 81 valid contents of each byte position, against base-4 digits."""
+    ks = _TERNARY_BYTE_K[byte]
+    for v in range(81):
+        digits = [(v // 3 ** j) % 3 for j in range(4)]      # code c in {0,1,2}
+        t = -np.ones((1, 16), dtype=np.int8)                 # c = 0 elsewhere
+        for k, c in zip(ks, digits):
+            t[0, k] = c - 1
+        p = oracle.pack_ternary(t)[0]
+        expect = sum(c << (2 * j) for j, c in enumerate(digits))
+        assert p[byte] == expect
+        assert all(p[b] == 0 for b in range(4) if b != byte)
+        # no field ever holds the invalid value 3
+        assert all(((p[byte] >> (2 * j)) & 3) != 3 for j in range(4))
+
+
+_BINARY_BYTE_K = {0: list(range(0, 16, 2)), 1: list(range(16, 32, 2)),
+                  2: list(range(1, 16, 2)), 3: list(range(17, 32, 2))}
+
+
+@pytest.mark.parametrize("byte", [0, 1, 2, 3])
+def test_binary_every_byte(byte):
+    ks = _BINARY_BYTE_K[byte]
+    for v in range(256):
+        t = -np.ones((1, 32), dtype=np.int8)
+        for j, k in enumerate(ks):
+            if (v >> j) & 1:
+                t[0, k] = 1
+        p = oracle.pack_binary(t)[0]
+        assert p[byte] == v
+        assert all(p[b] == 0 for b in range(4) if b != byte)
+
+
+def test_pack_unpack_round_trip():
+    g = wl.generator(11)
+    for N, K in [(1, 16), (3, 128), (17, 384), (64, 1024)]:
+        t = wl.ternary_codes(g, N, K, 0.35)
+        p = oracle.pack_ternary(t)
+        assert p.shape == (N, K // 4) and p.dtype == np.uint8
+        back, bad = oracle.unpack_ternary(p, K)
+        assert bad == 0 and np.array_equal(back, t)
+    for N, K in [(1, 32), (5, 128), (33, 2048)]:
+        t = wl.binary_codes(g, N, K)
+        p = oracle.pack_binary(t)
+        assert p.shape == (N, K // 8)
+        assert np.array_equal(oracle.unpack_binary(p, K), t)
+
+
+def test_unpack_counts_invalid_code():
+    p = np.zeros((2, 8), dtype=np.uint8)          # all codes 0 -> t = -1
+    p[0, 0] = 0b11                                 # k=0 field = 3 (invalid)
+    p[1, 7] = 0b11000011                           # two invalid fields
+    t, bad = oracle.unpack_ternary(p, 32)
+    assert bad == 3
+    assert t[0, 0] == 0 and t[0, 1] == -1
+    assert set(np.unique(t)) <= {-1, 0}
+
+
+def test_pack_rejects_out_of_set_codes():
+    with pytest.raises(ValueError):
+        oracle.pack_ternary(np.full((1, 16), 2, dtype=np.int8))
+    with pytest.raises(ValueError):
+        oracle.pack_binary(np.zeros((1, 32), dtype=np.int8))
+
+
+# -------------------------------------------------------- storage / bits ---
+
+def test_storage_sizes_exact():
+    for N, K in [(3072, 3072), (9216, 3072), (3072, 9216), (18432, 3072), (3072, 12288)]:
+        assert oracle.packed_bytes("ternary", N, K) * 8 == 2 * N * K
+        assert oracle.packed_bytes("binary", N, K) * 8 == N * K
+        assert oracle.scale_bytes(N, K) == 2 * N * K // 128
+        t = np.zeros((2, K), dtype=np.int8)
+        assert oracle.pack_ternary(t).nbytes == 2 * K // 4
+        assert oracle.pack_binary(t + 1 - 2 * (t == 0)).nbytes == 2 * K // 8
+
+
+def test_effective_bits_match_printed_values():
+    # Binary: 1 bit + 16/128 bits of scale = 1.125 (printed on the hada.io page and
+    # in "量化数学" of the ai-engineering page). Storage of this library is the same.
+    N, K = 3072, 3072
+    bits_bin = (oracle.packed_bytes("binary", N, K) + oracle.scale_bytes(N, K)) * 8 / (N * K)
+    assert bits_bin == 1.125
+    # Ternary information rate log2(3) + 16/128 ~= 1.71 (printed), and INT2 storage
+    # is 2 + 16/128 = 2.125 bits (2 bits per ternary, printed on the tailorednewshub page).
+    assert round(math.log2(3) + 16 / 128, 2) == 1.71
+    bits_tern = (oracle.packed_bytes("ternary", N, K) + oracle.scale_bytes(N, K)) * 8 / (N * K)
+    assert bits_tern == 2.125
+    # Layer-level reductions printed on the ai-engineering page: 16/1.125 ~ 14x, 16/1.71 ~ 9.4x
+    assert round(16 / 1.125) == 14
+    assert round(16 / 1.71, 1) == 9.4
+
+
+def test_generated_code_entropy():
+    g = wl.generator(5)
+    t = wl.ternary_codes(g, 512, 4096, None)
+    p = np.array([(t == v).mean() for v in (-1, 0, 1)])
+    H = -(p * np.log2(p)).sum()
+    assert abs(H - math.log2(3)) < 1e-3
+    t = wl.ternary_codes(g, 512, 4096, 0.35)
+    assert abs((t == 0).mean() - 0.35) < 3e-3
+    assert set(np.unique(t)) == {-1, 0, 1}
+
+
+# ------------------------------------------------------- dequant / GEMM ---
+
+def test_dequantize_closed_form():
+    t = np.array([[1, 0, -1] * 128], dtype=np.int8)[:, :256]
+    s = np.array([[0.5, -3.0]], dtype=np.float16)
+    W = oracle.dequantize(t, s)
+    assert W[0, 0] == 0.5 and W[0, 1] == 0 and W[0, 2] == -0.5
+    assert np.all(W[0, 128:][t[0, 128:] == 1] == -3.0)
+    assert np.all(W[0, 128:][t[0, 128:] == -1] == 3.0)
+    # subnormal fp16 scale survives exactly
+    s2 = np.array([[np.float16(2.0 ** -24), 0.0]], dtype=np.float16)
+    W2 = oracle.dequantize(t, s2)
+    assert W2[0, 0] == 2.0 ** -24 and np.all(W2[0, 128:] == 0)
+
+
+def test_worked_example(golden_dir):
+    g = _golden(golden_dir, "worked_linear.json")
+    K = 128
+    x = np.zeros((2, K), dtype=np.float32)
+    x[0] = 1.0
+    x[1, 0::2] = 0.5
+    x[1, 1::2] = -0.25
+    t = np.zeros((3, K), dtype=np.int8)
+    t[0, :64] = 1
+    t[0, 64:] = -1
+    t[1, 5], t[1, 6] = 1, -1
+    t[2, 0::2] = 1
+    s = np.array([[0.25], [2.0], [0.125]], dtype=np.float16)
+    b = np.array([1.0, -1.0, 0.5], dtype=np.float16)
+    for xd in ("f16", "bf16"):
+        xb = wl.to_bits(x, xd)
+        A = oracle.linear(xb, xd, t, s, b)
+        assert np.array_equal(A, np.array(g["Y"]))
+        assert np.array_equal(oracle.magnitude(xb, xd, t, s, b), np.array(g["Mag"]))
+        for yd in ("f16", "bf16", "f32"):
+            assert np.array_equal(oracle.decode(oracle.encode(A, yd), yd), A)
+
+
+def _exact(xb, xd, t, s, b):
+    """Exact rational value of one output element via fractions (brute force)."""
+    X = oracle.decode(xb, xd)
+    S = s.astype(np.float64)
+    M, K = X.shape
+    N = t.shape[0]
+    out = np.empty((M, N), dtype=object)
+    for m in range(M):
+        for n in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                acc += Fraction(float(X[m, k])) * Fraction(float(S[n, k // 128])) * int(t[n, k])
+            if b is not None:
+                acc += Fraction(float(b[n]))
+            out[m, n] = acc
+    return out
+
+
+@pytest.mark.parametrize("xd", ["f16", "bf16"])
+@pytest.mark.parametrize("K", [128, 256])
+def test_linear_against_exact_rationals(xd, K):
+    g = wl.generator(21 + K)
+    M, N = 3, 4
+    xb = wl.activations(g, M, K, xd, std=3.0)
+    t = wl.ternary_codes(g, N, K, 0.35)
+    s = wl.group_scales(g, N, K)
+    b = wl.bias_f16(g, N)
+    A = oracle.linear(xb, xd, t, s, b)
+    E = _exact(xb, xd, t, s, b)
+    Mg = oracle.magnitude(xb, xd, t, s, b)
+    for m in range(M):
+        for n in range(N):
+            err = abs(Fraction(float(A[m, n])) - E[m, n])
+            assert err <= Fraction(K * 2.0 ** -52) * Fraction(float(Mg[m, n]))
+    # sum|x w| against brute force too
+    X = oracle.decode(xb, xd)
+    W = s.astype(np.float64).repeat(128, axis=1) * t
+    for m in range(M):
+        for n in range(N):
+            ref = math.fsum(abs(X[m, k] * W[n, k]) for k in range(K)) + abs(float(b[n]))
+            assert abs(Mg[m, n] - ref) <= 1e-12 * ref
+
+
+def test_special_cases():
+    g = wl.generator(7)
+    M, N, K = 5, 6, 256
+    xb = wl.activations(g, M, K, "bf16")
+    X = oracle.decode(xb, "bf16")
+    b = wl.bias_f16(g, N)
+    s = wl.group_scales(g, N, K)
+    # t == 0 -> Y = bias exactly
+    A = oracle.linear(xb, "bf16", np.zeros((N, K), np.int8), s, b)
+    assert np.array_equal(A, np.broadcast_to(b.astype(np.float64), (M, N)))
+    # identity codes, unit scales -> selection of the first N columns of X
+    t = np.zeros((N, K), np.int8)
+    t[np.arange(N), np.arange(N)] = 1
+    A = oracle.linear(xb, "bf16", t, np.ones((N, K // 128), np.float16))
+    assert np.array_equal(A, X[:, :N])
+    # all +1 -> s * row sum per group; binary all -1 -> minus that
+    ones = np.ones((N, K), np.int8)
+    A = oracle.linear(xb, "bf16", ones, s)
+    G = X.reshape(M, K // 128, 128).sum(axis=2)        # per-group row sums
+    R = G @ s.astype(np.float64).T
+    assert np.allclose(A, R, rtol=1e-13, atol=1e-13)
+    A2 = oracle.linear(xb, "bf16", -ones, s)
+    assert np.allclose(A2, -R, rtol=1e-13, atol=1e-13)
+    # doubling every scale doubles the output exactly
+    t = wl.ternary_codes(g, N, K, 0.35)
+    A1 = oracle.linear(xb, "bf16", t, s)
+    A2 = oracle.linear(xb, "bf16", t, (s.astype(np.float32) * 2).astype(np.float16))
+    assert np.array_equal(A2, 2 * A1)
+    # a group whose scale is zero contributes nothing
+    s0 = s.copy()
+    s0[:, 1] = 0
+    A0 = oracle.linear(xb, "bf16", t, s0)
+    A_first = oracle.linear(xb[:, :128].copy(), "bf16", t[:, :128], s[:, :1])
+    assert np.allclose(A0, A_first, rtol=1e-13, atol=1e-13)
+
+
+def test_f32_gemm_meets_the_bound():
+    """An FP32-accumulated GEMM of the dequantised weights (what the method
+    specifies) lands inside the tolerance around the near-exact oracle value."""
+    g = wl.generator(9)
+    M, N, K = 64, 96, 3072
+    xb = wl.activations(g, M, K, "bf16")
+    t = wl.ternary_codes(g, N, K, 0.35)
+    s = wl.group_scales(g, N, K)
+    A = oracle.linear(xb, "bf16", t, s)
+    Mg = oracle.magnitude(xb, "bf16", t, s)
+    X32 = oracle.decode(xb, "bf16").astype(np.float32)
+    W32 = oracle.dequantize(t, s).astype(np.float32)
+    Y32 = (X32 @ W32.T).astype(np.float64)
+    ok, worst, _ = oracle.check(Y32, A, Mg, "f32")
+    assert ok and worst < 0.1
+
+
+# --------------------------------------------------- rounding / tolerance ---
+
+def test_bf16_rounding_literals(golden_dir):
+    for val, hexbits, _why in _golden(golden_dir, "bf16_rounding.json")["cases"]:
+        got = oracle.encode(np.array([float(val)]), "bf16")[0]
+        assert got == int(hexbits, 16), (val, hex(got), hexbits)
+
+
+def test_f16_rounding_matches_numpy():
+    g = wl.generator(3)
+    v = np.concatenate([
+        g.standard_normal(20000) * 10.0 ** g.integers(-9, 5, 20000),
+        (np.arange(-2000, 2000) + 0.5) * 2.0 ** -24,          # ties in the subnormal range
+        np.array([65504.0, 65519.99, 65520.0, -65520.0, 0.0, -0.0]),
+    ])
+    mine = oracle.encode(v, "f16")
+    ref = v.astype(np.float16).view(np.uint16)
+    assert np.array_equal(mine, ref)
+
+
+def test_bf16_rounding_matches_f32_route_on_f32_values():
+    # For values already in float32 the direct rounding equals the usual
+    # add-0x7FFF-plus-lsb bit trick on the float32 pattern.
+    g = wl.generator(4)
+    v = (g.standard_normal(50000) * 10.0 ** g.integers(-30, 30, 50000)).astype(np.float32)
+    u = v.view(np.uint32).astype(np.uint64)
+    trick = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    assert np.array_equal(oracle.encode(v.astype(np.float64), "bf16"), trick)
+
+
+def test_ulp_values():
+    assert oracle.ulp(np.array([1.0]), "bf16")[0] == 2.0 ** -7
+    assert oracle.ulp(np.array([1.0]), "f16")[0] == 2.0 ** -10
+    assert oracle.ulp(np.array([0.0]), "f16")[0] == 2.0 ** -24
+    assert oracle.ulp(np.array([3.0]), "bf16")[0] == 2.0 ** -6
+
+
+def test_gelu_table_values(golden_dir):
+    for x, y in _golden(golden_dir, "gelu_values.json")["cases"]:
+        assert abs(oracle.gelu(np.array([x]))[0] - y) <= 1e-15 * max(1.0, abs(y))
+    x = np.linspace(-6, 6, 101)
+    assert np.allclose(oracle.gelu(-x), oracle.gelu(x) - x, atol=1e-14)
+
+
+def test_check_detects_planted_errors():
+    g = wl.generator(8)
+    M, N, K = 8, 16, 256
+    xb = wl.activations(g, M, K, "bf16")
+    t = wl.ternary_codes(g, N, K, 0.35)
+    s = wl.group_scales(g, N, K)
+    A = oracle.linear(xb, "bf16", t, s)
+    Mg = oracle.magnitude(xb, "bf16", t, s)
+    Y = oracle.decode(oracle.encode(A, "bf16"), "bf16")
+    assert oracle.check(Y, A, Mg, "bf16")[0]
+    # a dropped term, a flipped sign or a transposed operand must all fail
+    t_drop = t.copy()
+    t_drop[:, 0] = 0
+    t_drop[t[:, 0] == 0, 0] = 1
+    for wrong in (oracle.linear(xb, "bf16", t_drop, s), -A, A + 0.01 * Mg):
+        assert not oracle.check(wrong, A, Mg, "f32")[0]
+    Ynan = Y.copy()
+    Ynan[0, 0] = np.nan
+    assert not oracle.check(Ynan, A, Mg, "bf16")[0]
