@@ -1,0 +1,269 @@
+"""Benchmark of the gfx950 low-bit-weight GEMM on one MI355X.
+
+One step = the ternary MLP pair of a 1024x1024 denoising step at 4608 tokens
+(4096 image + 512 text): X bf16 [4608 x 3072] -> up-proj [9216 x 3072] with the
+exact-erf GELU fused into its epilogue -> down-proj [3072 x 9216], group-128
+fp16 scales. Inputs are seeded synthetic data, resident in HBM before timing;
+the one-time packing is not in the step.
+
+Printed: ONE JSON line with TFLOP/s of the step (value), the roofline object of
+the dominant kernel (the large-M MFMA GEMM; per-launch time from HIP events on
+the launch stream), the CPU oracle timed on a bounded sample (cpu_baseline),
+and the small-M weight-streaming GB/s over a 100-linear MMDiT weight set at
+M = 16 and M = 1 (small_m).
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu] [--no-small]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ternary W×A16 GEMM TFLOP/s + % MFMA peak at M=4608; GB/s % HBM peak at M≤16"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_large_config3_traffic.json")
+
+
+def kernel_source_sha() -> str:
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "common.h"):
+        with open(os.path.join(ROOT, "bit_weight_gemm_int2_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic():
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def dev16(torch, bits, dtype):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(dtype)
+
+
+def bench_large(torch, lb, steps, warmup):
+    import workloads as wl
+    up, down = wl.config3()
+    M, K1, N1, N2 = up.M, up.K, up.N, down.N
+    x = dev16(torch, up.x, torch.bfloat16)
+    pu = lb.pack_ternary(torch.from_numpy(up.codes).cuda())
+    su = dev16(torch, up.scales, torch.float16)
+    pd = lb.pack_ternary(torch.from_numpy(down.codes).cuda())
+    sd = dev16(torch, down.scales, torch.float16)
+    h = torch.empty((M, N1), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((M, N2), dtype=torch.bfloat16, device="cuda")
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record()
+        lb.gemm(x, pu, su, "ternary", activation="gelu", out=h)
+        if evs is not None:
+            evs[1].record()
+        lb.gemm(h, pd, sd, "ternary", out=y)
+        if evs is not None:
+            evs[2].record()
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for i in range(steps):
+        step(evs[i])
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t0.elapsed_time(t1)
+    launches = []
+    for e in evs:
+        launches.append(e[0].elapsed_time(e[1]))
+        launches.append(e[1].elapsed_time(e[2]))
+    flop_launch = 2.0 * M * N1 * K1                     # == 2 * M * N2 * K2
+    flop_step = 2 * flop_launch
+    avg_launch_ms = float(np.mean(launches))
+    up_ms = float(np.mean(launches[0::2]))
+    down_ms = float(np.mean(launches[1::2]))
+    return dict(M=M, N1=N1, K1=K1, N2=N2, total_ms=total_ms, wall_s=wall, flop_step=flop_step,
+                flop_launch=flop_launch, avg_launch_ms=avg_launch_ms, up_ms=up_ms, down_ms=down_ms)
+
+
+def bench_small(torch, lb, reps=10):
+    """Weight streaming at M = 16 and M = 1 over the 100 ternary linears of one
+    transformer pass (and the 1-bit equivalent). One code matrix is drawn per
+    distinct shape and copied into its own device buffer per linear, so every
+    launch streams distinct memory (about 0.75 GB ternary, 0.4 GB binary, far
+    above the 256 MB last-level cache)."""
+    import workloads as wl
+    shapes = wl.mmdit_linear_shapes()
+    distinct = sorted({(N, K) for _, N, K in shapes})
+    out = {}
+    for fmt in ("ternary", "binary"):
+        g = wl.generator(4 if fmt == "ternary" else 5)
+        base = {}
+        for (N, K) in distinct:
+            codes = wl.ternary_codes(g, N, K, 0.35) if fmt == "ternary" else wl.binary_codes(g, N, K)
+            c = torch.from_numpy(codes).cuda()
+            p = lb.pack_ternary(c) if fmt == "ternary" else lb.pack_binary(c)
+            del c
+            base[(N, K)] = (p, dev16(torch, wl.group_scales(g, N, K), torch.float16))
+        layers = [(base[(N, K)][0].clone(), base[(N, K)][1].clone(), N, K) for _, N, K in shapes]
+        del base
+        gx = wl.generator(6)
+        for M in (16, 1):
+            xs = {K: dev16(torch, wl.activations(gx, M, K, "bf16"), torch.bfloat16)
+                  for K in sorted({K for _, _, K in shapes})}
+            ys = [torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for _, _, N, _ in layers]
+            wss = {}
+            for p, s, N, K in layers:
+                nb = lb.workspace_bytes(fmt, M, N, K)
+                if nb and nb > wss.get("n", 0):
+                    wss["n"] = nb
+            ws = torch.empty(max(wss.get("n", 16), 16), dtype=torch.uint8, device="cuda")
+
+            def sweep():
+                for (p, s, N, K), yy in zip(layers, ys):
+                    lb.gemm(xs[K], p, s, fmt, out=yy, workspace=ws)
+            sweep()
+            torch.cuda.synchronize()
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            t0.record()
+            for _ in range(reps):
+                sweep()
+            t1.record()
+            torch.cuda.synchronize()
+            ms = t0.elapsed_time(t1) / reps
+            wbytes = sum(lb.packed_bytes(fmt, N, K) + 2 * N * K // 128 for _, _, N, K in layers)
+            io = sum(2 * M * K + 2 * M * N for _, _, N, K in layers)
+            gbs = (wbytes + io) / (ms * 1e-3) / 1e9
+            out[f"{fmt}_M{M}"] = dict(ms_per_pass=round(ms, 4), bytes_per_pass=wbytes + io,
+                                      GBps=round(gbs, 1), frac_hbm_peak=round(gbs / PEAK_HBM_GBS, 4),
+                                      launches=len(layers))
+            del ys, xs, ws
+        del layers
+        torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(seconds_target=10.0):
+    """The oracle as it stands (float64 dequantise + BLAS matmul) on a bounded
+    sample of the step: the first R rows of the MLP pair (R grown up to all 4608),
+    repeated until about `seconds_target` seconds of CPU work are timed."""
+    import oracle
+    import workloads as wl
+    up, down = wl.config3()
+    cores = len(os.sched_getaffinity(0))
+
+    def one(rows):
+        A = oracle.linear(up.x[:rows], "bf16", up.codes, up.scales)
+        H = oracle.encode(oracle.gelu(A), "bf16")
+        oracle.linear(H, "bf16", down.codes, down.scales)
+
+    rows = 64
+    while True:
+        t0 = time.perf_counter()
+        one(rows)
+        dt = time.perf_counter() - t0
+        if dt > seconds_target / 3 or rows >= up.M:
+            break
+        rows = min(up.M, rows * 4)
+    reps, total = 1, dt
+    while total < seconds_target:
+        t0 = time.perf_counter()
+        one(rows)
+        total += time.perf_counter() - t0
+        reps += 1
+    flop = reps * (2.0 * rows * up.N * up.K + 2.0 * rows * down.N * down.K)
+    return dict(value=round(flop / total / 1e12, 6), unit="TFLOP/s", cores=cores, kind="oracle",
+                sample=f"{reps} pass(es) of the first {rows} of 4608 rows through up-proj, GELU and "
+                       f"down-proj (float64 oracle, {total:.1f} s)")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-small", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the low-bit linear layer runs on a single "
+              "device here (see the sharding notes in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bit_weight_gemm_int2_amd as lb
+    if not torch.cuda.is_available():
+        print("no GPU available", file=sys.stderr)
+        sys.exit(1)
+    lb.lib()
+
+    r = bench_large(torch, lb, args.steps, args.warmup)
+    ms_step = r["total_ms"] / args.steps
+    tflops = r["flop_step"] / (ms_step * 1e-3) / 1e12
+    achieved = r["flop_launch"] / (r["avg_launch_ms"] * 1e-3) / 1e12
+    traffic = load_traffic()
+    small = None if args.no_small else bench_small(torch, lb)
+    cpu = None if args.no_cpu else cpu_baseline()
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "ternary MLP pair of a 1024x1024 step: X bf16 [4608x3072] -> up [9216x3072] "
+                        "+ fused exact GELU -> down [3072x9216], INT2 codes P(0)=0.35, fp16 scales per 128",
+            "M": r["M"], "hidden": r["K1"], "mlp": r["N1"], "group": 128,
+            "frac_mfma_peak": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "up_ms": round(r["up_ms"], 4), "down_ms": round(r["down_ms"], 4),
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "kernel": "gemm_large_kernel<bf16, ternary>",
+            "avg_launch_ms": round(r["avg_launch_ms"], 4),
+            "flop_per_launch": r["flop_launch"],
+        },
+        "cpu_baseline": cpu,
+        "small_m": small,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

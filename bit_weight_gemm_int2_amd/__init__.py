@@ -1,0 +1,184 @@
+"""Python binding of ``liblowbit.so``, the gfx950 low-bit-weight GEMM library.
+
+Argument marshalling only: every step runs in the HIP kernels of the library.
+PyTorch supplies device memory (``torch.empty`` on the GPU) and the current
+HIP stream. If the library is not built, or no gfx950 GPU is present, calls
+raise; there is no fallback implementation.
+
+    packed = pack_ternary(codes_int8_cuda)            # [N, K/4] uint8
+    y = gemm(x_bf16_cuda, packed, scales_f16_cuda, "ternary", bias=None)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "liblowbit.so")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_GROUP, ERR_WORKSPACE, ERR_DEVICE, ERR_HIP = range(9)
+F16, BF16, F32, NONE = 0, 1, 2, 3
+BINARY, TERNARY = 1, 2
+ACT_NONE, ACT_GELU = 0, 1
+GROUP = 128
+
+_FMT = {"ternary": TERNARY, "binary": BINARY, TERNARY: TERNARY, BINARY: BINARY}
+_DT = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
+_ACT = {None: ACT_NONE, "none": ACT_NONE, "gelu": ACT_GELU, ACT_NONE: ACT_NONE, ACT_GELU: ACT_GELU}
+
+_lib = None
+
+# (name, restype, argtypes) for every entry point of include/lowbit.h
+_P, _I32, _I64, _SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+SIGNATURES = [
+    ("lowbit_abi_version", _I32, []),
+    ("lowbit_status_string", ctypes.c_char_p, [_I32]),
+    ("lowbit_init", _I32, []),
+    ("lowbit_packed_bytes", _I64, [_I32, _I64, _I64]),
+    ("lowbit_scale_count", _I64, [_I64, _I64, _I32]),
+    ("pack_ternary", _I32, [_P, _I64, _I64, _P, _P, _P]),
+    ("pack_binary", _I32, [_P, _I64, _I64, _P, _P, _P]),
+    ("unpack_lowbit", _I32, [_I32, _P, _I64, _I64, _P, _P, _P]),
+    ("lowbit_gemm_workspace_bytes", _SZ, [_I32, _I64, _I64, _I64]),
+    ("lowbit_gemm", _I32, [_I32, _P, _I32, _I64, _I64, _I64, _P, _P, _I32, _I64,
+                           _P, _I32, _P, _I32, _I64, _I32, _P, _SZ, _P]),
+    ("lowbit_gelu", _I32, [_P, _P, _I32, _I64, _P]),
+]
+
+
+class LowbitError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load liblowbit.so (built in-tree); raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run `python -m bit_weight_gemm_int2_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, res, args in SIGNATURES:
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().lowbit_status_string(status).decode()
+
+
+def _check(status: int, what: str):
+    if status != OK:
+        raise LowbitError(status, what)
+
+
+def _stream(stream=None) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _cuda(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+
+
+def packed_bytes(fmt, N: int, K: int) -> int:
+    return int(lib().lowbit_packed_bytes(_FMT[fmt], N, K))
+
+
+def workspace_bytes(fmt, M: int, N: int, K: int) -> int:
+    return int(lib().lowbit_gemm_workspace_bytes(_FMT[fmt], M, N, K))
+
+
+def _pack(fn, codes: torch.Tensor, div: int, check: bool, stream) -> torch.Tensor:
+    _cuda(codes, "codes")
+    if codes.dtype != torch.int8 or codes.dim() != 2:
+        raise ValueError("codes must be a 2-D int8 tensor")
+    codes = codes.contiguous()
+    N, K = codes.shape
+    out = torch.empty((N, K // div), dtype=torch.uint8, device=codes.device)
+    cnt = torch.empty(1, dtype=torch.int32, device=codes.device) if check else None
+    _check(fn(codes.data_ptr(), N, K, out.data_ptr(), _ptr(cnt), _stream(stream)), fn.__name__)
+    if check:
+        bad = int(cnt.item())
+        if bad:
+            raise ValueError(f"{bad} code(s) outside the allowed set")
+    return out
+
+
+def pack_ternary(codes: torch.Tensor, check: bool = True, stream=None) -> torch.Tensor:
+    """int8 codes [N, K] in {-1,0,+1} -> packed uint8 [N, K/4] (K % 16 == 0)."""
+    return _pack(lib().pack_ternary, codes, 4, check, stream)
+
+
+def pack_binary(codes: torch.Tensor, check: bool = True, stream=None) -> torch.Tensor:
+    """int8 codes [N, K] in {-1,+1} -> packed uint8 [N, K/8] (K % 32 == 0)."""
+    return _pack(lib().pack_binary, codes, 8, check, stream)
+
+
+def unpack(fmt, packed: torch.Tensor, K: int, stream=None) -> Tuple[torch.Tensor, int]:
+    """packed [N, K/4 or K/8] -> (int8 codes [N, K], number of invalid codes)."""
+    _cuda(packed, "packed")
+    packed = packed.contiguous()
+    N = packed.shape[0]
+    codes = torch.empty((N, K), dtype=torch.int8, device=packed.device)
+    cnt = torch.empty(1, dtype=torch.int32, device=packed.device)
+    _check(lib().unpack_lowbit(_FMT[fmt], packed.data_ptr(), N, K, codes.data_ptr(), cnt.data_ptr(),
+                               _stream(stream)), "unpack_lowbit")
+    return codes, int(cnt.item())
+
+
+def gemm(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, fmt, bias: Optional[torch.Tensor] = None,
+         out_dtype: Optional[torch.dtype] = None, activation=None, out: Optional[torch.Tensor] = None,
+         workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Y = act(X W^T + bias) with W = scale_g * t from packed codes.
+
+    x: [M, K] fp16/bf16 (row stride may exceed K); packed: [N, K/4] (ternary) or
+    [N, K/8] (binary) uint8; scales: fp16 [N, K/128]; bias: [N] or None.
+    Output dtype defaults to x's dtype."""
+    for t, nm in ((x, "x"), (packed, "packed"), (scales, "scales")):
+        _cuda(t, nm)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit stride along K")
+    M, K = x.shape
+    N = packed.shape[0]
+    packed = packed.contiguous()
+    scales = scales.contiguous()
+    if scales.dtype != torch.float16:
+        raise ValueError("scales must be float16")
+    odt = out_dtype or x.dtype
+    if out is None:
+        out = torch.empty((M, N), dtype=odt, device=x.device)
+    ws_need = workspace_bytes(fmt, M, N, K)
+    if ws_need and (workspace is None or workspace.numel() * workspace.element_size() < ws_need):
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=x.device)
+    st = lib().lowbit_gemm(
+        _FMT[fmt], x.data_ptr(), _DT[x.dtype], M, K, x.stride(0),
+        packed.data_ptr(), scales.data_ptr(), GROUP, N,
+        _ptr(bias), NONE if bias is None else _DT[bias.dtype],
+        out.data_ptr(), _DT[out.dtype], out.stride(0), _ACT[activation],
+        _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    _check(st, "lowbit_gemm")
+    return out
+
+
+def gelu(x: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Exact-erf GELU (x * Phi(x)) in FP32, stored in x's dtype."""
+    _cuda(x, "x")
+    x = x.contiguous()
+    out = torch.empty_like(x) if out is None else out
+    _check(lib().lowbit_gelu(x.data_ptr(), out.data_ptr(), _DT[x.dtype], x.numel(), _stream(stream)),
+           "lowbit_gelu")
+    return out

@@ -1,0 +1,215 @@
+// C ABI of the low-bit-weight GEMM library: argument validation, device
+// checks, plan selection and launches on the caller's stream. See
+// include/lowbit.h for the contract of every entry point.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/lowbit.h"
+#include "common.h"
+
+namespace lowbit {
+hipError_t launch_pack(int fmt, const int8_t* codes, int64_t N, int64_t K, uint8_t* packed,
+                       int32_t* counter, hipStream_t st);
+hipError_t launch_unpack(int fmt, const uint8_t* packed, int64_t N, int64_t K, int8_t* codes,
+                         int32_t* counter, hipStream_t st);
+hipError_t launch_gemm(int fmt, bool x_bf16, GemmArgs a, int num_cu, int variant, hipStream_t st);
+hipError_t launch_gelu(const void* in, void* out, int dtype, int64_t count, hipStream_t st);
+size_t small_workspace_bytes(int M, int N, int K, int num_cu);
+int small_m_limit();
+}  // namespace lowbit
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+struct DeviceInfo {
+  std::atomic<int> state{0};   // 0 unknown, 1 ok, 2 not gfx950
+  int num_cu = 0;
+};
+DeviceInfo g_dev[kMaxDevices];
+std::mutex g_mu;
+
+// Returns LOWBIT_OK and the CU count of the current device, or an error.
+int32_t current_device(int* num_cu) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LOWBIT_ERR_DEVICE;
+  DeviceInfo& d = g_dev[dev];
+  int s = d.state.load(std::memory_order_acquire);
+  if (s == 0) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    s = d.state.load(std::memory_order_relaxed);
+    if (s == 0) {
+      hipDeviceProp_t prop;
+      if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return LOWBIT_ERR_DEVICE;
+      bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+      d.num_cu = prop.multiProcessorCount;
+      s = ok ? 1 : 2;
+      d.state.store(s, std::memory_order_release);
+    }
+  }
+  if (s != 1) return LOWBIT_ERR_DEVICE;
+  if (num_cu) *num_cu = d.num_cu;
+  return LOWBIT_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int force_variant() {
+  const char* v = std::getenv("LOWBIT_FORCE_VARIANT");
+  if (!v) return 0;
+  if (!std::strcmp(v, "large")) return 1;
+  if (!std::strcmp(v, "small")) return 2;
+  return 0;
+}
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;
+
+}  // namespace
+
+extern "C" {
+
+int32_t lowbit_abi_version(void) { return LOWBIT_ABI_VERSION; }
+
+const char* lowbit_status_string(int32_t s) {
+  switch (s) {
+    case LOWBIT_OK: return "ok";
+    case LOWBIT_ERR_NULL: return "a required pointer is NULL";
+    case LOWBIT_ERR_SHAPE: return "bad shape (sizes must be >= 1 and < 2^31; K must follow the format rule)";
+    case LOWBIT_ERR_ALIGN: return "misaligned pointer or leading dimension";
+    case LOWBIT_ERR_DTYPE: return "unsupported dtype, format or activation";
+    case LOWBIT_ERR_GROUP: return "unsupported group size (only 128)";
+    case LOWBIT_ERR_WORKSPACE: return "workspace missing or too small";
+    case LOWBIT_ERR_DEVICE: return "current device is not a gfx950 GPU";
+    case LOWBIT_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int32_t lowbit_init(void) { return current_device(nullptr); }
+
+int64_t lowbit_packed_bytes(int32_t format, int64_t N, int64_t K) {
+  if (N < 1 || K < 1 || N >= kMaxDim || K >= kMaxDim) return -1;
+  if (format == LOWBIT_TERNARY_INT2) return K % 16 ? -1 : N * (K / 4);
+  if (format == LOWBIT_BINARY_1BIT) return K % 32 ? -1 : N * (K / 8);
+  return -1;
+}
+
+int64_t lowbit_scale_count(int64_t N, int64_t K, int32_t group) {
+  if (group != LOWBIT_GROUP || N < 1 || K < 1 || K % group) return -1;
+  return N * (K / group);
+}
+
+static int32_t pack_common(int fmt, const int8_t* codes, int64_t N, int64_t K, uint8_t* packed,
+                           int32_t* invalid_count, void* stream) {
+  if (!codes || !packed) return LOWBIT_ERR_NULL;
+  if (lowbit_packed_bytes(fmt, N, K) < 0) return LOWBIT_ERR_SHAPE;
+  if (!aligned(codes, 16) || !aligned(packed, 16) || (invalid_count && !aligned(invalid_count, 4)))
+    return LOWBIT_ERR_ALIGN;
+  int32_t st = current_device(nullptr);
+  if (st) return st;
+  hipError_t e = lowbit::launch_pack(fmt == LOWBIT_TERNARY_INT2 ? lowbit::FMT_TERNARY : lowbit::FMT_BINARY,
+                                     codes, N, K, packed, invalid_count, (hipStream_t)stream);
+  return e == hipSuccess ? LOWBIT_OK : LOWBIT_ERR_HIP;
+}
+
+int32_t pack_ternary(const int8_t* codes, int64_t N, int64_t K, uint8_t* packed,
+                     int32_t* invalid_count, void* stream) {
+  return pack_common(LOWBIT_TERNARY_INT2, codes, N, K, packed, invalid_count, stream);
+}
+
+int32_t pack_binary(const int8_t* codes, int64_t N, int64_t K, uint8_t* packed,
+                    int32_t* invalid_count, void* stream) {
+  return pack_common(LOWBIT_BINARY_1BIT, codes, N, K, packed, invalid_count, stream);
+}
+
+int32_t unpack_lowbit(int32_t format, const uint8_t* packed, int64_t N, int64_t K, int8_t* codes,
+                      int32_t* invalid_count, void* stream) {
+  if (format != LOWBIT_TERNARY_INT2 && format != LOWBIT_BINARY_1BIT) return LOWBIT_ERR_DTYPE;
+  if (!codes || !packed) return LOWBIT_ERR_NULL;
+  if (lowbit_packed_bytes(format, N, K) < 0) return LOWBIT_ERR_SHAPE;
+  if (!aligned(codes, 16) || !aligned(packed, 16) || (invalid_count && !aligned(invalid_count, 4)))
+    return LOWBIT_ERR_ALIGN;
+  int32_t st = current_device(nullptr);
+  if (st) return st;
+  hipError_t e = lowbit::launch_unpack(format == LOWBIT_TERNARY_INT2 ? lowbit::FMT_TERNARY : lowbit::FMT_BINARY,
+                                       packed, N, K, codes, invalid_count, (hipStream_t)stream);
+  return e == hipSuccess ? LOWBIT_OK : LOWBIT_ERR_HIP;
+}
+
+size_t lowbit_gemm_workspace_bytes(int32_t format, int64_t M, int64_t N, int64_t K) {
+  if (format != LOWBIT_TERNARY_INT2 && format != LOWBIT_BINARY_1BIT) return 0;
+  if (M < 1 || N < 1 || K < 128 || K % 128 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return 0;
+  int num_cu = 0;
+  if (current_device(&num_cu)) return 0;
+  int variant = force_variant();
+  bool small = variant == 2 || (variant == 0 && M <= lowbit::small_m_limit());
+  if (!small || M > 16) return 0;
+  return lowbit::small_workspace_bytes((int)M, (int)N, (int)K, num_cu);
+}
+
+int32_t lowbit_gemm(int32_t format, const void* X, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx,
+                    const uint8_t* W_packed, const void* scales, int32_t group, int64_t N,
+                    const void* bias, int32_t bias_dtype, void* Y, int32_t y_dtype, int64_t ldy,
+                    int32_t activation, void* workspace, size_t workspace_bytes, void* stream) {
+  if (format != LOWBIT_TERNARY_INT2 && format != LOWBIT_BINARY_1BIT) return LOWBIT_ERR_DTYPE;
+  if (x_dtype != LOWBIT_F16 && x_dtype != LOWBIT_BF16) return LOWBIT_ERR_DTYPE;
+  if (y_dtype != LOWBIT_F16 && y_dtype != LOWBIT_BF16 && y_dtype != LOWBIT_F32) return LOWBIT_ERR_DTYPE;
+  if (bias_dtype != LOWBIT_NONE && bias_dtype != LOWBIT_F16 && bias_dtype != LOWBIT_BF16 &&
+      bias_dtype != LOWBIT_F32)
+    return LOWBIT_ERR_DTYPE;
+  if (activation != LOWBIT_ACT_NONE && activation != LOWBIT_ACT_GELU_ERF) return LOWBIT_ERR_DTYPE;
+  if (group != LOWBIT_GROUP) return LOWBIT_ERR_GROUP;
+  if (!X || !W_packed || !scales || !Y) return LOWBIT_ERR_NULL;
+  if ((bias == nullptr) != (bias_dtype == LOWBIT_NONE)) return bias ? LOWBIT_ERR_DTYPE : LOWBIT_ERR_NULL;
+  if (M < 1 || N < 1 || K < 128 || K % 128 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim)
+    return LOWBIT_ERR_SHAPE;
+  if (ldx < K || ldy < N) return LOWBIT_ERR_SHAPE;
+  const size_t ysz = y_dtype == LOWBIT_F32 ? 4 : 2;
+  if (!aligned(X, 16) || !aligned(W_packed, 16) || !aligned(scales, 2) || !aligned(Y, ysz) || ldx % 8)
+    return LOWBIT_ERR_ALIGN;
+  if (bias && !aligned(bias, bias_dtype == LOWBIT_F32 ? 4 : 2)) return LOWBIT_ERR_ALIGN;
+  int num_cu = 0;
+  int32_t st = current_device(&num_cu);
+  if (st) return st;
+  size_t need = lowbit_gemm_workspace_bytes(format, M, N, K);
+  if (need && (!workspace || workspace_bytes < need)) return LOWBIT_ERR_WORKSPACE;
+  if (need && !aligned(workspace, 16)) return LOWBIT_ERR_ALIGN;
+
+  lowbit::GemmArgs a{};
+  a.X = (const uint16_t*)X;
+  a.ldx = ldx;
+  a.W = W_packed;
+  a.S = (const uint16_t*)scales;
+  a.bias = bias;
+  a.bias_dtype = bias_dtype;
+  a.Y = Y;
+  a.ldy = ldy;
+  a.y_dtype = y_dtype;
+  a.act = activation;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.ws = (float*)workspace;
+  int variant = force_variant();
+  if (variant == 2 && M > 16) variant = 1;
+  hipError_t e = lowbit::launch_gemm(format == LOWBIT_TERNARY_INT2 ? lowbit::FMT_TERNARY : lowbit::FMT_BINARY,
+                                     x_dtype == LOWBIT_BF16, a, num_cu, variant, (hipStream_t)stream);
+  return e == hipSuccess ? LOWBIT_OK : LOWBIT_ERR_HIP;
+}
+
+int32_t lowbit_gelu(const void* in, void* out, int32_t dtype, int64_t count, void* stream) {
+  if (!in || !out) return LOWBIT_ERR_NULL;
+  if (dtype != LOWBIT_F16 && dtype != LOWBIT_BF16 && dtype != LOWBIT_F32) return LOWBIT_ERR_DTYPE;
+  if (count < 1) return LOWBIT_ERR_SHAPE;
+  if (!aligned(in, 16) || !aligned(out, 16)) return LOWBIT_ERR_ALIGN;
+  int32_t st = current_device(nullptr);
+  if (st) return st;
+  hipError_t e = lowbit::launch_gelu(in, out, dtype, count, (hipStream_t)stream);
+  return e == hipSuccess ? LOWBIT_OK : LOWBIT_ERR_HIP;
+}
+
+}  // extern "C"

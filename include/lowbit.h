@@ -1,0 +1,165 @@
+/*
+ * lowbit.h - C ABI of the MI355X (gfx950) low-bit-weight linear layer.
+ *
+ * The layer is the one the Bonsai Image 4B pages describe for the diffusion
+ * transformer: every weight is w = scale_g * t, with t in {-1, 0, +1}
+ * (ternary, stored with 2 bits per value, "INT2") or t in {-1, +1} (binary,
+ * 1 bit per value), and one FP16 scale shared by each group of 128 weights
+ * ("Como Bonsai Ternary 4B revoluciona la difusion texto-imagen", section
+ * "Representacion y almacenamiento de los pesos ternarios"; "Bonsai Image 4B
+ * 1-bit untuk pembuatan gambar di perangkat lokal", section on the two
+ * variants). Activations are FP16 or BF16.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every data pointer is a DEVICE pointer owned by the caller. The library
+ *    never allocates, frees or synchronises; work is enqueued on `stream`
+ *    (a hipStream_t; NULL means the null stream) and runs asynchronously.
+ *  - The return value reports argument errors (checked on the host before any
+ *    launch) and launch errors (hipGetLastError after the launch). Errors
+ *    that happen later on the device surface at the caller's next
+ *    synchronisation, as for any HIP kernel.
+ *  - Matrices are row-major. Sizes are element counts unless stated.
+ *  - The library runs on gfx950 only; other devices get LOWBIT_ERR_DEVICE.
+ *  - Every call is stateless apart from a per-device cache of device
+ *    properties, and is safe to call from several host threads.
+ *
+ * Packed weight layout (this library's own; the pages fix only "2 bits per
+ * ternary" and "1 bit per binary weight")
+ * ---------------------------------------------------------------------------
+ *  A packed matrix has N rows; row n is a run of little-endian 32-bit words
+ *  along K, rows stored back to back (row stride K/4 bytes ternary, K/8
+ *  bytes binary).
+ *  Ternary: code c = t + 1 in {0,1,2} (3 is invalid). Word u of a row holds
+ *    k = 16u .. 16u+15; the code of k = 16u + 2i + h (i = 0..7, h = 0/1) sits
+ *    at bits [16h + 2i, 16h + 2i + 1]: even k fill the low half word, odd k
+ *    the high half word.
+ *  Binary: bit b = 1 means t = +1, 0 means t = -1. Word u holds
+ *    k = 32u .. 32u+31; the bit of k = 32u + 2i + h (i = 0..15) sits at
+ *    bit 16h + i.
+ *  Scales: FP16, shape [N, K/128], row-major; scale[n, g] covers
+ *    k = 128g .. 128g+127 of output row n. Any finite value is allowed
+ *    (zero and subnormal included); non-finite scales give unspecified results.
+ */
+#ifndef LOWBIT_H
+#define LOWBIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LOWBIT_ABI_VERSION 1
+#define LOWBIT_GROUP 128
+
+typedef enum {
+  LOWBIT_OK = 0,
+  LOWBIT_ERR_NULL = 1,       /* a required pointer is NULL                      */
+  LOWBIT_ERR_SHAPE = 2,      /* a size is < 1, too large, or K breaks its rule  */
+  LOWBIT_ERR_ALIGN = 3,      /* a pointer or leading dimension breaks alignment */
+  LOWBIT_ERR_DTYPE = 4,      /* unsupported dtype / format / activation code    */
+  LOWBIT_ERR_GROUP = 5,      /* group size other than 128                       */
+  LOWBIT_ERR_WORKSPACE = 6,  /* workspace missing or smaller than required      */
+  LOWBIT_ERR_DEVICE = 7,     /* current device is not gfx950, or no device      */
+  LOWBIT_ERR_HIP = 8         /* the HIP runtime reported an error               */
+} lowbit_status;
+
+typedef enum { LOWBIT_F16 = 0, LOWBIT_BF16 = 1, LOWBIT_F32 = 2, LOWBIT_NONE = 3 } lowbit_dtype;
+typedef enum { LOWBIT_BINARY_1BIT = 1, LOWBIT_TERNARY_INT2 = 2 } lowbit_format;
+typedef enum { LOWBIT_ACT_NONE = 0, LOWBIT_ACT_GELU_ERF = 1 } lowbit_activation;
+
+/* ABI version of the loaded library (LOWBIT_ABI_VERSION). */
+int32_t lowbit_abi_version(void);
+
+/* Human-readable text for a status code; never NULL, static storage. */
+const char* lowbit_status_string(int32_t status);
+
+/* Check that the current device is gfx950 and cache its properties.
+ * Optional: every entry point does the same on first use. */
+int32_t lowbit_init(void);
+
+/* Bytes of packed codes for an N x K matrix: N*K/4 (ternary), N*K/8 (binary);
+ * -1 for a bad format or a K that breaks the packing rule (ternary K % 16,
+ * binary K % 32) or N, K < 1. */
+int64_t lowbit_packed_bytes(int32_t format, int64_t N, int64_t K);
+
+/* Number of FP16 scales, N * K / group; -1 if group != 128 or K % group != 0. */
+int64_t lowbit_scale_count(int64_t N, int64_t K, int32_t group);
+
+/* Pack int8 ternary codes t[N][K] in {-1,0,+1} into the INT2 layout above
+ * (the 2-bit storage of "Representacion y almacenamiento de los pesos
+ * ternarios"). codes: N*K bytes, 16-byte aligned. packed: N*K/4 bytes,
+ * 16-byte aligned, must not overlap codes. K % 16 == 0.
+ * invalid_count (nullable, device int32, 4-byte aligned): set to the number
+ * of input bytes outside {-1,0,+1}; such values are packed as code 1 (t = 0).
+ * Output bytes are a pure function of the input: bit-identical on every run. */
+int32_t pack_ternary(const int8_t* codes, int64_t N, int64_t K, uint8_t* packed,
+                     int32_t* invalid_count, void* stream);
+
+/* Pack int8 binary codes t[N][K] in {-1,+1} into the 1-bit layout above
+ * (1 bit per binary weight, as on the hada.io page and in the "1.125 bits"
+ * arithmetic of the ai-engineering page). packed: N*K/8 bytes. K % 32 == 0.
+ * Values other than -1/+1 are counted in invalid_count and packed as bit 0
+ * (t = -1). Alignment and ownership as pack_ternary. */
+int32_t pack_binary(const int8_t* codes, int64_t N, int64_t K, uint8_t* packed,
+                    int32_t* invalid_count, void* stream);
+
+/* Inverse of the packers: packed (format layout above) -> int8 codes[N][K].
+ * Ternary code 3 is invalid: it decodes to 0 and is counted in
+ * invalid_count (nullable). Binary has no invalid pattern (count set to 0). */
+int32_t unpack_lowbit(int32_t format, const uint8_t* packed, int64_t N, int64_t K,
+                      int8_t* codes, int32_t* invalid_count, void* stream);
+
+/* Workspace bytes lowbit_gemm needs for this problem (0 when none). Depends
+ * only on (format, M, N, K) and the current device. */
+size_t lowbit_gemm_workspace_bytes(int32_t format, int64_t M, int64_t N, int64_t K);
+
+/* The low-bit linear layer (w = scale_g * t from "Representacion y
+ * almacenamiento de los pesos ternarios", applied as Y = X W^T):
+ *
+ *   Y[m, n] = act( sum_k X[m, k] * float(scales[n, k/128]) * t[n, k] + bias[n] )
+ *
+ * with FP32 accumulation, then one round-to-nearest-even cast to y_dtype.
+ * Accuracy contract per element: |Y - exact| <= 1e-3 * (sum_k |x_k w_k| +
+ * |bias|) + 1e-5, plus half an output ulp for FP16/BF16 outputs (before the
+ * activation; GELU is then applied to the FP32 value).
+ *
+ *   format      LOWBIT_TERNARY_INT2 or LOWBIT_BINARY_1BIT
+ *   X           [M][ldx] of x_dtype (LOWBIT_F16 or LOWBIT_BF16); 16-byte
+ *               aligned, ldx >= K, ldx % 8 == 0
+ *   W_packed    [N][K/4] or [N][K/8] bytes in the packed layout, 16-byte aligned
+ *   scales      FP16 [N][K/group], 2-byte aligned; group must be 128
+ *   bias        nullable; [N] of bias_dtype (F16, BF16, F32), or
+ *               bias_dtype = LOWBIT_NONE with bias = NULL
+ *   Y           [M][ldy] of y_dtype (F16, BF16, F32); aligned to its element
+ *               size, ldy >= N; must not overlap X, W, scales, bias
+ *   activation  LOWBIT_ACT_NONE or LOWBIT_ACT_GELU_ERF (x * Phi(x), exact erf)
+ *   workspace   device scratch of at least lowbit_gemm_workspace_bytes();
+ *               may be NULL when that is 0. Must not be shared by calls that
+ *               can run concurrently.
+ *   M, N, K     M, N >= 1; K >= 128 and K % 128 == 0; M, N, K < 2^31
+ *
+ * Codes equal to 3 in a ternary matrix are not checked here (hot path); the
+ * result for them is unspecified. The result is deterministic: the same
+ * inputs give the same bits on every call on the same device. */
+int32_t lowbit_gemm(int32_t format,
+                    const void* X, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx,
+                    const uint8_t* W_packed, const void* scales, int32_t group, int64_t N,
+                    const void* bias, int32_t bias_dtype,
+                    void* Y, int32_t y_dtype, int64_t ldy,
+                    int32_t activation,
+                    void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* Exact-erf GELU, y = x * Phi(x), computed in FP32, elementwise over `count`
+ * values of `dtype` (F16, BF16 or F32); in and out may be the same buffer and
+ * must be 16-byte aligned. The activation the 1024x1024 MLP pair applies
+ * between its two linears when it is not fused into the first one. */
+int32_t lowbit_gelu(const void* in, void* out, int32_t dtype, int64_t count, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LOWBIT_H */

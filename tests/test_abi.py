@@ -1,0 +1,101 @@
+"""The C-ABI library loads and exports every entry point include/lowbit.h declares;
+host-only calls (sizes, status strings, argument checks that fail before any
+device work) behave as documented. CPU only: no kernel is launched here."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lowbit.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s+(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    import bit_weight_gemm_int2_amd as b
+    if not os.path.exists(b.LIB_PATH):
+        b_build = __import__("bit_weight_gemm_int2_amd.build", fromlist=["build"])
+        b_build.build()
+    return b.lib()
+
+
+def test_header_declares_expected_entry_points():
+    names = _declared()
+    for want in ("pack_ternary", "pack_binary", "unpack_lowbit", "lowbit_gemm",
+                 "lowbit_gemm_workspace_bytes", "lowbit_packed_bytes", "lowbit_scale_count",
+                 "lowbit_status_string", "lowbit_abi_version", "lowbit_init", "lowbit_gelu"):
+        assert want in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    import bit_weight_gemm_int2_amd as b
+    out = subprocess.run(["nm", "-D", "--defined-only", b.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in _declared():
+        assert name in exported, name
+        assert hasattr(L, name)
+    # the Python binding declares a signature for every one of them
+    assert sorted(n for n, _, _ in b.SIGNATURES) == _declared()
+
+
+def test_host_only_queries(L):
+    import bit_weight_gemm_int2_amd as b
+    assert L.lowbit_abi_version() == 1
+    assert L.lowbit_packed_bytes(b.TERNARY, 3072, 3072) == 3072 * 3072 // 4
+    assert L.lowbit_packed_bytes(b.BINARY, 9216, 3072) == 9216 * 3072 // 8
+    assert L.lowbit_packed_bytes(b.TERNARY, 4, 24) == -1       # K % 16
+    assert L.lowbit_packed_bytes(b.BINARY, 4, 48) == -1        # K % 32
+    assert L.lowbit_packed_bytes(7, 4, 128) == -1
+    assert L.lowbit_scale_count(3072, 9216, 128) == 3072 * 72
+    assert L.lowbit_scale_count(3072, 9216, 64) == -1
+    for s in range(9):
+        assert len(L.lowbit_status_string(s)) > 0
+    assert L.lowbit_status_string(99) == b"unknown status"
+
+
+def test_argument_errors_before_any_device_work(L):
+    """Every status that the host check returns before touching the device."""
+    import bit_weight_gemm_int2_amd as b
+    P = 1 << 20            # fake, 16-byte-aligned non-NULL "device" address
+    good = dict(fmt=b.TERNARY, X=P, xd=b.BF16, M=16, K=256, ldx=256, W=P, S=P, group=128, N=64,
+                bias=None, bd=b.NONE, Y=P, yd=b.BF16, ldy=64, act=0, ws=None, wsb=0)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return L.lowbit_gemm(a["fmt"], a["X"], a["xd"], a["M"], a["K"], a["ldx"], a["W"], a["S"],
+                             a["group"], a["N"], a["bias"], a["bd"], a["Y"], a["yd"], a["ldy"],
+                             a["act"], a["ws"], a["wsb"], None)
+
+    assert call(fmt=3) == b.ERR_DTYPE
+    assert call(xd=b.F32) == b.ERR_DTYPE
+    assert call(yd=b.NONE) == b.ERR_DTYPE
+    assert call(bd=9) == b.ERR_DTYPE
+    assert call(act=5) == b.ERR_DTYPE
+    assert call(group=64) == b.ERR_GROUP
+    assert call(X=None) == b.ERR_NULL
+    assert call(W=None) == b.ERR_NULL
+    assert call(bd=b.F16) == b.ERR_NULL                       # bias dtype without bias
+    assert call(bias=P) == b.ERR_DTYPE                        # bias without dtype
+    assert call(K=200, ldx=200) == b.ERR_SHAPE                # K % 128
+    assert call(M=0) == b.ERR_SHAPE
+    assert call(N=0) == b.ERR_SHAPE
+    assert call(ldx=128) == b.ERR_SHAPE                       # ldx < K
+    assert call(ldy=32) == b.ERR_SHAPE
+    assert call(X=P + 8) == b.ERR_ALIGN
+    assert call(ldx=260) == b.ERR_ALIGN
+    assert call(Y=P + 2, yd=b.F32) == b.ERR_ALIGN
+    assert call(S=P + 1) == b.ERR_ALIGN
+    assert L.pack_ternary(None, 4, 16, P, None, None) == b.ERR_NULL
+    assert L.pack_ternary(P, 4, 24, P, None, None) == b.ERR_SHAPE
+    assert L.pack_binary(P + 4, 4, 32, P, None, None) == b.ERR_ALIGN
+    assert L.unpack_lowbit(5, P, 4, 32, P, None, None) == b.ERR_DTYPE
+    assert L.lowbit_gelu(None, P, b.BF16, 10, None) == b.ERR_NULL
+    assert L.lowbit_gelu(P, P, b.NONE, 10, None) == b.ERR_DTYPE

@@ -1,0 +1,248 @@
+"""GPU GEMM parity against the CPU oracle, element by element, within the stated
+tolerance |d| <= 1e-3 * sum_k |x_k w_k| + 1e-5 (+ half an output ulp for
+16-bit outputs); bit-exact where every partial sum is exact in FP32."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from gpu_util import TORCH_DT, banner, dev_bits, dev_weights, oracle_linear, run_linear, to_host64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lb():
+    import bit_weight_gemm_int2_amd as b
+    b.lib()
+    return b
+
+
+def _assert_parity(Y, A, Mg, y_dtype, what):
+    ok, worst, nfail = oracle.check(Y, A, Mg, y_dtype)
+    assert ok, f"{what}: {nfail} elements outside the bound, worst ratio {worst:.3g}"
+    return worst
+
+
+@pytest.fixture
+def force_variant():
+    old = os.environ.get("LOWBIT_FORCE_VARIANT")
+
+    def set_(v):
+        if v is None:
+            os.environ.pop("LOWBIT_FORCE_VARIANT", None)
+        else:
+            os.environ["LOWBIT_FORCE_VARIANT"] = v
+    yield set_
+    set_(old)
+
+
+# ------------------------------------------------------------- workloads ---
+
+def test_config1_ternary_f16(lb):
+    banner("gemm config1 64x256x256 f16")
+    lin = wl.config1()
+    Y, _ = run_linear(lin)
+    A, Mg = oracle_linear(lin)
+    _assert_parity(Y, A, Mg, "f16", "config1")
+
+
+def test_config2_ternary_bf16_bias(lb):
+    banner("gemm config2 1536x3072x3072 bf16 + bias")
+    lin = wl.config2()
+    Y, _ = run_linear(lin)
+    A, Mg = oracle_linear(lin)
+    _assert_parity(Y, A, Mg, "bf16", "config2")
+
+
+@pytest.mark.parametrize("M", [1536, 16, 1])
+def test_config4_binary(lb, M):
+    banner(f"gemm config4 binary M={M}")
+    for lin in wl.config4(M):
+        Y, _ = run_linear(lin)
+        A, Mg = oracle_linear(lin)
+        _assert_parity(Y, A, Mg, "bf16", lin.name)
+
+
+def test_config3_mlp_pair(lb):
+    """Up-proj with fused GELU, the standalone GELU kernel, and the down-proj fed
+    with the oracle's own bf16 GELU output; rows sampled for the oracle."""
+    banner("gemm config3 MLP pair 4608x9216x3072 / 4608x3072x9216")
+    up, down = wl.config3()
+    rows = np.sort(wl.generator(77).choice(up.M, 384, replace=False))
+    rows = np.concatenate([rows, [0, up.M - 1]])
+    x = dev_bits(up.x, "bf16")
+    pu, su = dev_weights("ternary", up.codes, up.scales)
+    pre = lb.gemm(x, pu, su, "ternary")                       # bf16, no activation
+    h_fused = lb.gemm(x, pu, su, "ternary", activation="gelu")
+    h_split = lb.gelu(pre)
+    torch.cuda.synchronize()
+    A, Mg = oracle.linear(up.x[rows], "bf16", up.codes, up.scales), None
+    Mg = oracle.magnitude(up.x[rows], "bf16", up.codes, up.scales)
+    _assert_parity(to_host64(pre)[rows], A, Mg, "bf16", "up")
+    # GELU: |GELU(a') - GELU(a)| <= max|GELU'| * |a' - a|, max|GELU'| < 1.13
+    G = oracle.gelu(A)
+    for name, h in (("fused", h_fused), ("split", h_split)):
+        H = to_host64(h)[rows]
+        lim = 1.13 * (oracle.REL_TOL * Mg + oracle.ABS_TOL) + 0.5 * oracle.ulp(np.maximum(abs(G), abs(H)), "bf16") \
+            + 4 * oracle.ulp(G, "f32")
+        if name == "split":   # GELU of the bf16-rounded pre-activation: one more bf16 half ulp inside
+            lim = lim + 1.13 * 0.5 * oracle.ulp(A, "bf16")
+        bad = np.abs(H - G) > lim
+        assert not bad.any(), f"GELU {name}: {bad.sum()} elements out of bound"
+    # down-proj on the oracle's bf16 GELU output (all rows of H from the oracle)
+    Hb = oracle.encode(oracle.gelu(oracle.linear(up.x, "bf16", up.codes, up.scales)), "bf16")
+    Yd = lb.gemm(dev_bits(Hb, "bf16"), *dev_weights("ternary", down.codes, down.scales), "ternary")
+    torch.cuda.synchronize()
+    A2 = oracle.linear(Hb[rows], "bf16", down.codes, down.scales)
+    Mg2 = oracle.magnitude(Hb[rows], "bf16", down.codes, down.scales)
+    _assert_parity(to_host64(Yd)[rows], A2, Mg2, "bf16", "down")
+
+
+# --------------------------------------------------------- random shapes ---
+
+_SHAPES = [(1, 1, 128), (5, 15, 256), (16, 64, 384), (17, 130, 128), (100, 300, 1024),
+           (130, 129, 256), (257, 64, 512), (64, 513, 640), (33, 1000, 2048)]
+
+
+@pytest.mark.parametrize("i,shape", list(enumerate(_SHAPES)))
+@pytest.mark.parametrize("fmt", ["ternary", "binary"])
+def test_random_shapes(lb, i, shape, fmt):
+    M, N, K = shape
+    xd = ("bf16", "f16")[i % 2]
+    yd = ("bf16", "f16", "f32")[i % 3]
+    with_bias = i % 2 == 1
+    lin = wl.make_linear(f"rand{i}", fmt, M, N, K, x_dtype=xd, y_dtype=yd, seed=100 + i,
+                         p0=0.35, with_bias=with_bias)
+    Y, _ = run_linear(lin)
+    A, Mg = oracle_linear(lin)
+    _assert_parity(Y, A, Mg, yd, f"{fmt} {shape} {xd}->{yd}")
+
+
+# ------------------------------------------------------------ exact cases ---
+
+@pytest.mark.parametrize("fmt", ["ternary", "binary"])
+@pytest.mark.parametrize("M", [3, 16, 200])
+def test_exact_arithmetic_is_bit_exact(lb, fmt, M):
+    """Small integer activations and power-of-two scales: every partial sum is an
+    exactly representable FP32 value, so any summation order gives the oracle's
+    value bit for bit."""
+    g = wl.generator(300 + M)
+    N, K = 96, 256
+    x = g.integers(-8, 9, size=(M, K)).astype(np.float32)
+    t = wl.ternary_codes(g, N, K, 0.35) if fmt == "ternary" else wl.binary_codes(g, N, K)
+    s = (2.0 ** g.integers(-6, 3, size=(N, K // 128))).astype(np.float16)
+    for xd in ("bf16", "f16"):
+        lin = wl.Linear("exact", fmt, M, N, K, xd, "f32", wl.to_bits(x, xd), t, s)
+        Y, _ = run_linear(lin)
+        A, _ = oracle_linear(lin)
+        assert np.array_equal(Y, A)
+
+
+def test_special_scales_and_codes(lb):
+    g = wl.generator(400)
+    M, N, K = 20, 70, 384
+    xb = wl.activations(g, M, K, "bf16")
+    t = wl.ternary_codes(g, N, K, 0.35)
+    s = wl.group_scales(g, N, K)
+    s[0, :] = 0                                        # all-zero row of scales
+    s[1, 1] = 0
+    s[2, :] = np.float16(2.0 ** -24)                   # smallest subnormal
+    s[3, 0] = np.float16(3.0 * 2.0 ** -20)             # another subnormal
+    s[4, :] = -s[4, :]                                 # negative scales
+    s[5, 2] = np.float16(60000.0)                      # large
+    b = wl.bias_f16(g, N)
+    lin = wl.Linear("special", "ternary", M, N, K, "bf16", "f32", xb, t, s, b)
+    Y, _ = run_linear(lin)
+    A, Mg = oracle_linear(lin)
+    _assert_parity(Y, A, Mg, "f32", "special scales")
+    assert np.all(Y[:, 0] == np.float32(b[0]))          # zero scales -> bias exactly
+    # all-zero codes -> output equals the bias exactly
+    lin0 = wl.Linear("zero", "ternary", M, N, K, "bf16", "bf16", xb, np.zeros_like(t), s, b)
+    Y0, _ = run_linear(lin0)
+    assert np.array_equal(Y0, np.broadcast_to(oracle.decode(oracle.encode(b.astype(np.float64), "bf16"), "bf16"), (M, N)))
+
+
+# ---------------------------------------------------- variants / safety ---
+
+@pytest.mark.parametrize("fmt", ["ternary", "binary"])
+@pytest.mark.parametrize("M,N,K", [(16, 3072, 3072), (7, 512, 9216), (1, 200, 12288)])
+def test_small_and_large_kernels_agree_with_oracle(lb, force_variant, fmt, M, N, K):
+    lin = wl.make_linear("both", fmt, M, N, K, seed=500 + M, p0=0.35)
+    A, Mg = oracle_linear(lin)
+    for v in ("small", "large"):
+        force_variant(v)
+        Y, _ = run_linear(lin)
+        _assert_parity(Y, A, Mg, "bf16", f"{v} kernel")
+
+
+@pytest.mark.parametrize("M", [4, 300])
+def test_deterministic_and_every_output_written(lb, M):
+    lin = wl.make_linear("det", "ternary", M, 777, 1280, seed=600 + M, p0=0.35)
+    x = dev_bits(lin.x, "bf16")
+    packed, s = dev_weights("ternary", lin.codes, lin.scales)
+    out1 = torch.full((M, 777), float("nan"), dtype=torch.float32, device="cuda")
+    out2 = torch.full((M, 777), float("nan"), dtype=torch.float32, device="cuda")
+    lb.gemm(x, packed, s, "ternary", out=out1)
+    lb.gemm(x, packed, s, "ternary", out=out2)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out1).any()
+    assert torch.equal(out1.view(torch.int32), out2.view(torch.int32))
+
+
+def test_strided_activation_and_output(lb):
+    """ldx > K and ldy > N: only the addressed region is read and written."""
+    g = wl.generator(700)
+    M, N, K = 40, 96, 256
+    lin = wl.make_linear("stride", "ternary", M, N, K, seed=701)
+    big = np.zeros((M, K + 64), dtype=np.uint16)
+    big[:, :K] = lin.x
+    x = dev_bits(big, "bf16")[:, :K]
+    packed, s = dev_weights("ternary", lin.codes, lin.scales)
+    yfull = torch.full((M, N + 8), 7.0, dtype=torch.bfloat16, device="cuda")
+    lb.gemm(x, packed, s, "ternary", out=yfull[:, :N])
+    torch.cuda.synchronize()
+    A, Mg = oracle_linear(lin)
+    _assert_parity(to_host64(yfull[:, :N].contiguous()), A, Mg, "bf16", "strided")
+    assert torch.all(yfull[:, N:] == 7.0)
+
+
+def test_gelu_kernel(lb):
+    g = wl.generator(800)
+    v = (g.standard_normal(100_000) * 3).astype(np.float32)
+    v[:5] = [0.0, -0.0, 10.0, -10.0, 1e-30]
+    for dt in ("bf16", "f16", "f32"):
+        if dt == "f32":
+            x = torch.from_numpy(v).cuda()
+            xin = v.astype(np.float64)
+        else:
+            bits = wl.to_bits(v, dt)
+            x = dev_bits(bits, dt)
+            xin = oracle.decode(bits, dt)
+        y = to_host64(lb.gelu(x))
+        ref = oracle.gelu(xin)
+        # FP32 erfc: relative error of a few 1e-7 where GELU is not tiny; in the far
+        # negative tail (x < -8, |GELU| < 1e-14) the device erfcf loses relative
+        # accuracy, so an absolute floor of 1e-6 applies (ten times below the 1e-5
+        # floor of the layer tolerance the activation feeds); then one cast
+        lim = 1e-6 * np.abs(ref) + 1e-6
+        if dt != "f32":
+            lim = lim + 0.5 * oracle.ulp(np.maximum(abs(ref), abs(y)), dt)
+        bad = np.flatnonzero(np.abs(y - ref) > lim)
+        assert bad.size == 0, (dt, [(float(xin[i]), float(y[i]), float(ref[i]), float(lim[i])) for i in bad[:5]])
+
+
+def test_device_side_errors(lb):
+    x = torch.zeros((4, 128), dtype=torch.bfloat16, device="cuda")
+    p = torch.zeros((4, 32), dtype=torch.uint8, device="cuda")
+    s = torch.zeros((4, 1), dtype=torch.float16, device="cuda")
+    y = torch.empty((4, 8), dtype=torch.bfloat16, device="cuda")     # ldy = 8 >= N
+    L = lb.lib()
+    need = L.lowbit_gemm_workspace_bytes(lb.TERNARY, 4, 4, 128)
+    st = L.lowbit_gemm(lb.TERNARY, x.data_ptr(), lb.BF16, 4, 128, 128, p.data_ptr(), s.data_ptr(), 128, 4,
+                       None, lb.NONE, y.data_ptr(), lb.BF16, 8, 0, None, 0, None)
+    assert st == lb.OK if need == 0 else st == lb.ERR_WORKSPACE
+    assert L.lowbit_init() == lb.OK
