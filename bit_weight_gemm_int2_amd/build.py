@@ -16,7 +16,11 @@ SOURCES = ["api.hip", "pack.hip", "gemm.hip"]
 
 # Packed FP32 VALU instructions are disabled for all device code; plain
 # float code is scheduled as scalar v_fma_f32 / v_mul_f32 instead.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# MFMA accumulators are kept in VGPRs (the per-group rescale of the large-M
+# kernel is VALU work on them; VALU instructions cannot read AGPRs), which
+# leaves the AGPR file to the MFMA A operands.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def hipcc() -> str:

@@ -10,14 +10,11 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 enum { DT_F16 = 0, DT_BF16 = 1, DT_F32 = 2, DT_NONE = 3 };
 enum { FMT_BINARY = 1, FMT_TERNARY = 2 };
 enum { ACT_NONE = 0, ACT_GELU = 1 };
-
-// Tag types for the activation element type.
-struct XBF16 { static constexpr bool bf16 = true; };
-struct XF16 { static constexpr bool bf16 = false; };
 
 struct GemmArgs {
   const uint16_t* X;   // [M][ldx] 16-bit activations
@@ -85,27 +82,53 @@ __device__ __forceinline__ void store_out(void* Y, int64_t ldy, int dtype, int m
 // ---------------------------------------------------------------------------
 // Code unpacking into MFMA operand registers.
 //
-// A 16x16x32 MFMA operand register holds two 16-bit values. The kernels feed
-// the MFMA with t/2 (ternary) or -t/2 (binary) instead of t: both are exact
-// in FP16 and BF16 and their low byte is zero, so one byte lookup (ternary)
-// or one sign-bit insert (binary) builds a value. The factor 2 (or -2) is
-// folded into the group scale, where it is exact.
+// An MFMA operand register holds two 16-bit values. The kernels feed the MFMA
+// with t/2 (ternary) or -t/2 (binary) instead of t: both are exact in FP16 and
+// BF16 and their low byte is zero, so one byte lookup (ternary) or one
+// sign-bit insert (binary) builds a value. The factor 2 (or -2) is folded into
+// the group scale, where it is exact.
 //
-// Ternary: after a right rotation the two codes of a register sit at bits
-// [9:8] and [25:24]; v_perm looks their high bytes up in a 3-entry table and
-// writes 0x00 into the low bytes (selector value 0x0C in bytes 0 and 2).
+// Ternary codes are the 2-bit two's complement of t (00 = 0, 01 = +1,
+// 11 = -1). After a right rotation the two codes of a register sit at bits
+// [9:8] and [25:24]; masking leaves a v_perm selector whose bytes 1 and 3 are
+// the codes and whose bytes 0 and 2 are zero. Byte 0 of the table is 0x00, so
+// the low bytes and t = 0 both read zero; bytes 1 and 3 hold the high bytes
+// of +0.5 and -0.5 (the invalid code 10 reads byte 2 = 0x00).
 // ---------------------------------------------------------------------------
 template <bool BF16>
 __device__ __forceinline__ constexpr uint32_t tern_table() {
-  // bytes 0,1,2 = high byte of -0.5, 0, +0.5 for code c = 0, 1, 2
-  return BF16 ? 0x003F00BFu : 0x003800B8u;
+  return BF16 ? 0xBF003F00u : 0xB8003800u;
 }
 
 template <bool BF16>
 __device__ __forceinline__ uint32_t tern_pair(uint32_t w, uint32_t rot) {
   uint32_t x = rot ? __builtin_amdgcn_alignbit(w, w, rot) : w;
-  uint32_t sel = (x & 0x03000300u) | 0x000C000Cu;   // bytes 0, 2: 0x0C = "0x00"
-  return __builtin_amdgcn_perm(0u, tern_table<BF16>(), sel);
+  return __builtin_amdgcn_perm(0u, tern_table<BF16>(), x & 0x03000300u);
+}
+
+// Variants with the table (ternary) or the sign mask and base (binary) passed
+// in registers, so a group whose scale is zero can use an all-zero table.
+__device__ __forceinline__ uint32_t tern_pair_t(uint32_t w, uint32_t rot, uint32_t table) {
+  uint32_t x = rot ? __builtin_amdgcn_alignbit(w, w, rot) : w;
+  return __builtin_amdgcn_perm(0u, table, x & 0x03000300u);
+}
+
+__device__ __forceinline__ u32x4 tern_chunk_t(uint32_t w, int c, uint32_t table) {
+  u32x4 r;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) r[v] = tern_pair_t(w, (uint32_t)((8 * (c & 1) + 2 * v + 24) & 31), table);
+  return r;
+}
+
+__device__ __forceinline__ u32x4 bin_chunk_t(uint32_t w, int c, uint32_t mask, uint32_t base) {
+  u32x4 r;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const uint32_t rot = (uint32_t)((4 * c + v + 17) & 31);
+    const uint32_t x = rot ? __builtin_amdgcn_alignbit(w, w, rot) : w;
+    r[v] = (x & mask) | base;
+  }
+  return r;
 }
 
 // Binary: after a right rotation the two bits of a register sit at bits 15
@@ -143,6 +166,16 @@ __device__ __forceinline__ u32x4 bin_chunk(uint32_t w, int c) {
 #pragma unroll
   for (int v = 0; v < 4; ++v) r[v] = bin_pair<BF16>(w, (uint32_t)((4 * c + v + 17) & 31));
   return r;
+}
+
+template <bool BF16>
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (BF16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
 template <bool BF16>

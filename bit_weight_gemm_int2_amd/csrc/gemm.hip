@@ -23,152 +23,181 @@
 namespace lowbit {
 
 // ===========================================================================
-// Large-M kernel: 128x128 output tile per workgroup, 4 waves of 64x64, one
-// 128-group (BK = 128) per pipeline stage, LDS double buffered.
-//   LDS A : activations, 128 rows x 128 k, row stride 136 (bank-spread)
-//   LDS B : packed codes kept packed: ternary [4 pair][128 n] x 8 bytes,
-//           binary [4][128 n] x 4 bytes
-//   LDS S : the FP32 factor +-2*scale per column
+// Large-M kernel (v_mfma_f32_32x32x16): a workgroup computes a 128 x 256 tile
+// of Y with 4 waves side by side along N, each wave 128 x 64 (4 x 2 blocks of
+// 32 x 32). One pipeline stage is one 128-group along K.
+//
+//  * Activations: global -> LDS with direct 16-byte LDS DMA loads
+//    (global_load_lds_dwordx4), three stages in flight. LDS holds each row's
+//    sixteen 16-byte chunks XOR-swizzled by (row % 16), which makes the
+//    fragment reads (32 rows, same chunk) bank-conflict free. Every wave reads
+//    the fragments of a whole group into registers (AGPRs, which MFMA reads
+//    directly); those of group g+1 replace those of group g while the second
+//    column block of group g is computed.
+//  * Packed codes and scales: straight from global memory into VGPRs (each
+//    wave owns distinct columns, so nothing is shared through LDS), one group
+//    ahead of use. A lane loads 16 bytes (ternary) or 8 bytes (binary): the
+//    64 codes its lane group contributes to the group.
+//  * Group scales, Horner form: the MFMAs accumulate in units of the current
+//    group's scale c_g = +-2 s_g, and at each group boundary the accumulator
+//    is rescaled by c_{g-1} / c_g (one FP32 multiply per element); after the
+//    last group it is multiplied by c_G. In exact arithmetic this is
+//    sum_g c_g P_g; in FP32 each rescale adds one rounding (about 2G ulps of
+//    relative error over the whole sum, far inside the 1e-3 tolerance). A
+//    group whose scale is zero is fed as zero codes and keeps the previous
+//    reference scale, so zero and subnormal scales are exact. Requires finite
+//    scales and |partial sums| < 2^100 (the quotient of two FP16 scales is at
+//    most 2^40, so a partial sum can grow by that much in accumulator units).
+//
+// K order inside a group: lane group q = lane / 32 owns k-local [64q, 64q+64);
+// MFMA step s (0..7) uses its slots 64q + 8s .. +7.
 // ===========================================================================
 namespace large {
-constexpr int BM = 128, BN = 128, AST = 136, THREADS = 256;
-}
+constexpr int BM = 128, BN = 256, THREADS = 256, STAGES = 3;
+constexpr int ROW_BYTES = 256;                 // 128 k x 2 bytes
+constexpr int STAGE_BYTES = BM * ROW_BYTES;    // 32 KiB
+}  // namespace large
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 template <bool BF16, int FMT>
-__global__ __launch_bounds__(256) void gemm_large_kernel(GemmArgs a) {
+__global__ __launch_bounds__(256, 1) void gemm_large_kernel(GemmArgs a, int tiles_m, int tiles_n) {
   using namespace large;
   constexpr bool TERN = FMT == FMT_TERNARY;
-  constexpr int BWORDS = TERN ? 8 : 4;               // packed words per row per group
-  __shared__ __align__(16) uint16_t sA[2][BM * AST];
-  __shared__ __align__(16) uint32_t sB[2][BWORDS * BN];
-  __shared__ float sS[2][BN];
+  __shared__ __align__(16) uint8_t sA[STAGES][STAGE_BYTES];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, q = lane >> 4, r16 = lane & 15;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int lane = tid & 63, q = lane >> 5, r32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // XCD-aware tile order: consecutive workgroups land on different XCDs, so
+  // give each XCD a contiguous range of tiles (N fastest) to share L2.
+  int t = blockIdx.x;
+  const int T = tiles_m * tiles_n;
+  if ((T & 7) == 0) t = (t & 7) * (T >> 3) + (t >> 3);
+  const int m0 = (t / tiles_n) * BM, n0 = (t % tiles_n) * BN;
   const int G = a.K >> 7;
-  const int64_t wrow = TERN ? (a.K >> 2) : (a.K >> 3);   // packed bytes per weight row
+  const int64_t wrow = TERN ? (a.K >> 2) : (a.K >> 3);
   const float factor = TERN ? 2.0f : -2.0f;
+  const uint32_t table = tern_table<BF16>();
+  const uint32_t bmask = 0x80008000u, bbase = BF16 ? 0x3F003F00u : 0x38003800u;
 
-  // ---- global -> register staging of one group ----
-  u32x4 ra[8];
-  u32x4 rb;
-  float rs = 0.0f;
-  auto gload = [&](int g) {
+  // ---- activation stage g -> LDS buffer `buf` (wave w: rows 32w .. 32w+31) ----
+  auto dma = [&](int g, int buf) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      int idx = tid + THREADS * i;
-      int row = idx >> 4, c16 = idx & 15;
-      int m = m0 + row;
-      if (m < a.M)
-        ra[i] = *(const u32x4*)(a.X + (int64_t)m * a.ldx + (g << 7) + c16 * 8);
-      else
-        ra[i] = u32x4{0u, 0u, 0u, 0u};
-    }
-    if (TERN) {
-      int row = tid >> 1, half = tid & 1, n = n0 + row;
-      if (n < a.N)
-        rb = *(const u32x4*)(a.W + (int64_t)n * wrow + g * 32 + half * 16);
-      else
-        rb = u32x4{0x55555555u, 0x55555555u, 0x55555555u, 0x55555555u};   // t = 0
-    } else if (tid < BN) {
-      int n = n0 + tid;
-      if (n < a.N)
-        rb = *(const u32x4*)(a.W + (int64_t)n * wrow + g * 16);
-      else
-        rb = u32x4{0u, 0u, 0u, 0u};
-    }
-    if (tid < BN) {
-      int n = n0 + tid;
-      rs = n < a.N ? factor * half_bits_to_float(a.S[(int64_t)n * G + g]) : 0.0f;
+    for (int it = 0; it < 8; ++it) {
+      const int rb = 32 * wave + 4 * it;                    // wave-uniform first row
+      const int r = rb + (lane >> 4);
+      const int c = (lane & 15) ^ (r & 15);                 // chunk stored in slot lane&15
+      const int m = min(m0 + r, a.M - 1);                   // rows past M: any valid row
+      const uint16_t* src = a.X + (int64_t)m * a.ldx + (g << 7) + 8 * c;
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr_t)(sA[buf] + rb * ROW_BYTES), 16, 0, 0);
     }
   };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      int idx = tid + THREADS * i;
-      int row = idx >> 4, c16 = idx & 15;
-      *(u32x4*)&sA[buf][row * AST + c16 * 8] = ra[i];
-    }
-    if (TERN) {
-      int row = tid >> 1, half = tid & 1;
-      u32x2* b2 = (u32x2*)sB[buf];
-      b2[(2 * half) * BN + row] = u32x2{rb[0], rb[1]};
-      b2[(2 * half + 1) * BN + row] = u32x2{rb[2], rb[3]};
-    } else if (tid < BN) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sB[buf][j * BN + tid] = rb[j];
-    }
-    if (tid < BN) sS[buf][tid] = rs;
+  auto afrag = [&](int buf, int i, int s) -> u32x4 {
+    const int r = 32 * i + r32;
+    const int p = (8 * q + s) ^ (r & 15);
+    return *(const u32x4*)(sA[buf] + r * ROW_BYTES + p * 16);
   };
 
-  f32x4 acc[4][4];
+  // ---- packed codes + scales of this lane's two columns ----
+  int ncol[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) ncol[j] = min(n0 + 64 * wave + 32 * j + r32, a.N - 1);
+  auto bload = [&](int g, u32x4 (&bw)[2], float (&sc)[2]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint8_t* p = a.W + (int64_t)ncol[j] * wrow;
+      if (TERN) {
+        bw[j] = *(const u32x4*)(p + g * 32 + 16 * q);
+      } else {
+        u32x2 v = *(const u32x2*)(p + g * 16 + 8 * q);
+        bw[j] = u32x4{v[0], v[1], 0u, 0u};
+      }
+      sc[j] = factor * half_bits_to_float(a.S[(int64_t)ncol[j] * G + g]);
+    }
+  };
+
+  f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+  float cref[2] = {1.0f, 1.0f};                 // reference scale of the accumulator
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
+  u32x4 A[4][8];
+  u32x4 bw[2];
+  float sc[2];
 
-  for (int g = 0; g < G; ++g) {
-    const int cur = g & 1;
-    if (g + 1 < G) gload(g + 1);
-
-    // packed words of this lane group for the wave's 4 column blocks
-    uint32_t w0[4], w1[4];
+  // one column block of one group: rescale to the group's scale, then 32 MFMAs
+  auto block = [&](int j, bool refill, int nbuf) {
+    const float s = sc[j];
+    const bool zero = s == 0.0f;
+    const float r = zero ? 1.0f : cref[j] / s;
+    cref[j] = zero ? cref[j] : s;
+    const uint32_t tb = zero ? 0u : table;
+    const uint32_t mk = zero ? 0u : bmask, bs = zero ? 0u : bbase;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int nl = wn * 64 + j * 16 + r16;
-      if (TERN) {
-        u32x2 v = ((const u32x2*)sB[cur])[q * BN + nl];
-        w0[j] = v[0];
-        w1[j] = v[1];
-      } else {
-        w0[j] = sB[cur][q * BN + nl];
-        w1[j] = 0u;
+    for (int i = 0; i < 4; ++i) acc[i][j] *= r;
+#pragma unroll
+    for (int st = 0; st < 8; ++st) {
+      const u32x4 bf = TERN ? tern_chunk_t(bw[j][st >> 1], st & 1, tb)
+                            : bin_chunk_t(bw[j][st >> 2], st & 3, mk, bs);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i][j] = mfma32<BF16>(A[i][st], bf, acc[i][j]);
+      if (refill) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) A[i][st] = afrag(nbuf, i, st);
       }
     }
-    f32x4 tmp[4][4];
+  };
+
+  // prologue: stages 0 and 1 in flight, group-0 codes, then group-0 fragments
+  dma(0, 0);
+  if (G > 1) dma(1, 1);
+  bload(0, bw, sc);
+  __builtin_amdgcn_s_waitcnt(0);        // own DMA + loads done
+  __syncthreads();
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      u32x4 af[4], bf[4];
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *(const u32x4*)&sA[cur][(wm * 64 + i * 16 + r16) * AST + 32 * q + 8 * c];
+    for (int st = 0; st < 8; ++st) A[i][st] = afrag(0, i, st);
+
+  for (int g = 0; g < G; ++g) {
+    const bool more = g + 1 < G;
+    u32x4 bwn[2];
+    float scn[2];
+    block(0, false, 0);
+    // pipeline point: stage g+1 landed everywhere; refill stage g+2
+    if (more) {
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      bload(g + 1, bwn, scn);
+      if (g + 2 < G) dma(g + 2, (g + 2) % STAGES);
+      block(1, true, (g + 1) % STAGES);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bf[j] = TERN ? tern_chunk<BF16>(w0[j], w1[j], c) : bin_chunk<BF16>(w0[j], c);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          tmp[i][j] = mfma16<BF16>(af[i], bf[j], c == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : tmp[i][j]);
+      for (int j = 0; j < 2; ++j) {
+        bw[j] = bwn[j];
+        sc[j] = scn[j];
+      }
+    } else {
+      block(1, false, 0);
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float s = sS[cur][wn * 64 + j * 16 + r16];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i][j] += s * tmp[i][j];
-    }
-    if (g + 1 < G) sstore(cur ^ 1);
-    __syncthreads();
   }
 
-  // ---- epilogue: bias, activation, one RNE cast, store ----
+  // ---- epilogue: final scale, bias, activation, one RNE cast, store ----
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    int n = n0 + wn * 64 + j * 16 + r16;
+  for (int j = 0; j < 2; ++j) {
+    const int n = n0 + 64 * wave + 32 * j + r32;
     if (n >= a.N) continue;
-    float b = a.bias ? load_bias(a.bias, a.bias_dtype, n) : 0.0f;
+    const float b = a.bias ? load_bias(a.bias, a.bias_dtype, n) : 0.0f;
+    const float c = cref[j];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        int m = m0 + wm * 64 + i * 16 + 4 * q + r;
-        if (m < a.M) store_out(a.Y, a.ldy, a.y_dtype, m, n, finish(acc[i][j][r], b, a.act));
+      for (int r = 0; r < 16; ++r) {
+        const int m = m0 + 32 * i + 8 * (r >> 2) + 4 * q + (r & 3);
+        if (m < a.M) store_out(a.Y, a.ldy, a.y_dtype, m, n, finish(acc[i][j][r] * c, b, a.act));
       }
   }
 }
@@ -349,8 +378,8 @@ static void launch_small_t(GemmArgs& a, const SmallPlan& p, hipStream_t st) {
 
 template <bool BF16, int FMT>
 static void launch_large_t(GemmArgs& a, hipStream_t st) {
-  dim3 grid((a.N + large::BN - 1) / large::BN, (a.M + large::BM - 1) / large::BM);
-  hipLaunchKernelGGL((gemm_large_kernel<BF16, FMT>), grid, dim3(large::THREADS), 0, st, a);
+  const int tm = (a.M + large::BM - 1) / large::BM, tn = (a.N + large::BN - 1) / large::BN;
+  hipLaunchKernelGGL((gemm_large_kernel<BF16, FMT>), dim3(tm * tn), dim3(large::THREADS), 0, st, a, tm, tn);
 }
 
 int small_m_limit() { return 16; }

@@ -23,11 +23,11 @@ __device__ __forceinline__ void count_invalid(int32_t* counter, int bad) {
   if ((threadIdx.x & 63) == __builtin_ctzll(m)) atomicAdd(counter, total);
 }
 
-// ternary value -> offset code, invalid values -> code 1 (t = 0)
+// ternary value -> 2-bit two's complement, invalid values -> code 0 (t = 0)
 __device__ __forceinline__ uint32_t tern_code(int8_t t, int& bad) {
   bool ok = (t >= -1) && (t <= 1);
   bad += ok ? 0 : 1;
-  return ok ? (uint32_t)(t + 1) : 1u;
+  return ok ? ((uint32_t)t & 3u) : 0u;
 }
 
 __global__ void pack_ternary_kernel(const int8_t* __restrict__ codes, uint32_t* __restrict__ out,
@@ -83,8 +83,8 @@ __global__ void unpack_ternary_kernel(const uint32_t* __restrict__ in, int8_t* _
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       uint32_t c = (x >> (16 * (j & 1) + 2 * (j >> 1))) & 3u;
-      bad += (c == 3u) ? 1 : 0;
-      int t = (c == 3u) ? 0 : (int)c - 1;
+      bad += (c == 2u) ? 1 : 0;                     // 10 is not a ternary code
+      int t = (c == 2u) ? 0 : ((int)(c << 30) >> 30);   // sign-extend the 2-bit field
       o[j >> 2] |= ((uint32_t)(uint8_t)(int8_t)t) << (8 * (j & 3));
     }
     *(u32x4*)(codes + 16 * w) = o;

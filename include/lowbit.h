@@ -30,7 +30,8 @@
  *  A packed matrix has N rows; row n is a run of little-endian 32-bit words
  *  along K, rows stored back to back (row stride K/4 bytes ternary, K/8
  *  bytes binary).
- *  Ternary: code c = t + 1 in {0,1,2} (3 is invalid). Word u of a row holds
+ *  Ternary: the code of t is its 2-bit two's complement (0 -> 00, +1 -> 01,
+ *    -1 -> 11; 10 is invalid). Word u of a row holds
  *    k = 16u .. 16u+15; the code of k = 16u + 2i + h (i = 0..7, h = 0/1) sits
  *    at bits [16h + 2i, 16h + 2i + 1]: even k fill the low half word, odd k
  *    the high half word.
@@ -93,7 +94,7 @@ int64_t lowbit_scale_count(int64_t N, int64_t K, int32_t group);
  * ternarios"). codes: N*K bytes, 16-byte aligned. packed: N*K/4 bytes,
  * 16-byte aligned, must not overlap codes. K % 16 == 0.
  * invalid_count (nullable, device int32, 4-byte aligned): set to the number
- * of input bytes outside {-1,0,+1}; such values are packed as code 1 (t = 0).
+ * of input bytes outside {-1,0,+1}; such values are packed as code 00 (t = 0).
  * Output bytes are a pure function of the input: bit-identical on every run. */
 int32_t pack_ternary(const int8_t* codes, int64_t N, int64_t K, uint8_t* packed,
                      int32_t* invalid_count, void* stream);
@@ -107,7 +108,7 @@ int32_t pack_binary(const int8_t* codes, int64_t N, int64_t K, uint8_t* packed,
                     int32_t* invalid_count, void* stream);
 
 /* Inverse of the packers: packed (format layout above) -> int8 codes[N][K].
- * Ternary code 3 is invalid: it decodes to 0 and is counted in
+ * Ternary code 10 is invalid: it decodes to 0 and is counted in
  * invalid_count (nullable). Binary has no invalid pattern (count set to 0). */
 int32_t unpack_lowbit(int32_t format, const uint8_t* packed, int64_t N, int64_t K,
                       int8_t* codes, int32_t* invalid_count, void* stream);
@@ -141,8 +142,7 @@ size_t lowbit_gemm_workspace_bytes(int32_t format, int64_t M, int64_t N, int64_t
  *               can run concurrently.
  *   M, N, K     M, N >= 1; K >= 128 and K % 128 == 0; M, N, K < 2^31
  *
- * Codes equal to 3 in a ternary matrix are not checked here (hot path); the
- * result for them is unspecified. The result is deterministic: the same
+ * Ternary codes 10 are not checked here (hot path); they act as t = 0. The result is deterministic: the same
  * inputs give the same bits on every call on the same device. */
 int32_t lowbit_gemm(int32_t format,
                     const void* X, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx,

@@ -21,7 +21,8 @@ What it computes, and where the pages say so
   ``x * s * t`` is exact in float64: 8 or 11 significand bits times 11 bits).
 
 Readings where the pages are silent (each is listed in the design notes):
-* INT2 code of a ternary value: ``c = t + 1`` in {0, 1, 2}; the value 3 is invalid.
+* INT2 code of a ternary value: the 2-bit two's complement of t, ``c = t & 3``:
+  0 -> 00, +1 -> 01, -1 -> 11; the pattern 10 is invalid.
 * Bit order: a packed row is a sequence of little-endian 32-bit words. Ternary:
   word ``u`` holds k = 16u .. 16u+15; the code of k = 16u + 2i + h (i in 0..7,
   h in {0, 1}) sits at bits [16h + 2i, 16h + 2i + 1]. Even k fill the low half
@@ -138,7 +139,7 @@ def pack_ternary(t: np.ndarray) -> np.ndarray:
         raise ValueError("ternary packing needs K % 16 == 0")
     if not np.isin(t, (-1, 0, 1)).all():
         raise ValueError("ternary codes must lie in {-1, 0, +1}")
-    c = (t.astype(np.int64) + 1).astype(np.uint32)          # offset code 0, 1, 2
+    c = (t.astype(np.int64) & 3).astype(np.uint32)          # 2-bit two's complement
     words = np.zeros((N, K // 16), dtype=np.uint32)
     for j in range(16):                                      # position inside the word
         i, h = divmod(j, 2)
@@ -165,7 +166,8 @@ def pack_binary(t: np.ndarray) -> np.ndarray:
 def unpack_ternary(packed: np.ndarray, K: int) -> Tuple[np.ndarray, int]:
     """uint8 [N, K/4] -> (int8 codes [N, K], number of invalid 2-bit fields).
 
-    An invalid field (value 3) decodes to 0 and is counted."""
+    A 2-bit field is read as a two's-complement number; the pattern 10 (-2) is
+    invalid, decodes to 0 and is counted."""
     packed = np.ascontiguousarray(packed, dtype=np.uint8)
     N = packed.shape[0]
     words = packed.reshape(N, K // 4).view("<u4").astype(np.uint32)
@@ -173,9 +175,10 @@ def unpack_ternary(packed: np.ndarray, K: int) -> Tuple[np.ndarray, int]:
     invalid = 0
     for j in range(16):
         i, h = divmod(j, 2)
-        c = (words >> np.uint32(16 * h + 2 * i)) & np.uint32(3)
-        invalid += int((c == 3).sum())
-        t[:, j::16] = np.where(c == 3, 0, c.astype(np.int64) - 1).astype(np.int8)
+        c = ((words >> np.uint32(16 * h + 2 * i)) & np.uint32(3)).astype(np.int64)
+        v = np.where(c >= 2, c - 4, c)                       # two's complement
+        invalid += int((v == -2).sum())
+        t[:, j::16] = np.where(v == -2, 0, v).astype(np.int8)
     return t, invalid
 
 

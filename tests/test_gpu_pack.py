@@ -52,11 +52,11 @@ def test_unpack_round_trip_and_invalid_codes(lb):
     p = torch.from_numpy(oracle.pack_ternary(t)).cuda()
     back, bad = lb.unpack("ternary", p, 512)
     assert bad == 0 and np.array_equal(back.cpu().numpy(), t)
-    # plant invalid 2-bit fields (value 3) in the packed bytes
+    # plant invalid 2-bit fields (pattern 10) in the packed bytes
     pb = oracle.pack_ternary(t)
-    pb[0, 0] |= 0b11
-    pb[5, 17] |= 0b11000000
-    pb[63, 127] = 0xFF
+    pb[0, 0] = (pb[0, 0] & 0xFC) | 0b10
+    pb[5, 17] = (pb[5, 17] & 0x3F) | 0b10000000
+    pb[63, 127] = 0xAA
     ref_t, ref_bad = oracle.unpack_ternary(pb, 512)
     back, bad = lb.unpack("ternary", torch.from_numpy(pb).cuda(), 512)
     assert bad == ref_bad and np.array_equal(back.cpu().numpy(), ref_t)

@@ -39,19 +39,21 @@ _TERNARY_BYTE_K = {0: [0, 2, 4, 6], 1: [8, 10, 12, 14], 2: [1, 3, 5, 7], 3: [9, 
 
 @pytest.mark.parametrize("byte", [0, 1, 2, 3])
 def test_ternary_every_valid_byte(byte):
-    """All 3^4 = 81 valid contents of each byte position, against base-4 digits."""
+    """All 3^4 = 81 valid contents of each byte position, against base-4 digits
+    of the 2-bit two's-complement codes (0 -> 0, +1 -> 1, -1 -> 3)."""
     ks = _TERNARY_BYTE_K[byte]
+    code = {0: 0, 1: 1, -1: 3}
     for v in range(81):
-        digits = [(v // 3 ** j) % 3 for j in range(4)]      # code c in {0,1,2}
-        t = -np.ones((1, 16), dtype=np.int8)                 # c = 0 elsewhere
-        for k, c in zip(ks, digits):
-            t[0, k] = c - 1
+        tvals = [(v // 3 ** j) % 3 - 1 for j in range(4)]   # t in {-1, 0, 1}
+        t = np.zeros((1, 16), dtype=np.int8)                 # code 0 elsewhere
+        for k, tv in zip(ks, tvals):
+            t[0, k] = tv
         p = oracle.pack_ternary(t)[0]
-        expect = sum(c << (2 * j) for j, c in enumerate(digits))
+        expect = sum(code[tv] << (2 * j) for j, tv in enumerate(tvals))
         assert p[byte] == expect
         assert all(p[b] == 0 for b in range(4) if b != byte)
-        # no field ever holds the invalid value 3
-        assert all(((p[byte] >> (2 * j)) & 3) != 3 for j in range(4))
+        # no field ever holds the invalid pattern 10
+        assert all(((p[byte] >> (2 * j)) & 3) != 2 for j in range(4))
 
 
 _BINARY_BYTE_K = {0: list(range(0, 16, 2)), 1: list(range(16, 32, 2)),
@@ -87,13 +89,16 @@ def test_pack_unpack_round_trip():
 
 
 def test_unpack_counts_invalid_code():
-    p = np.zeros((2, 8), dtype=np.uint8)          # all codes 0 -> t = -1
-    p[0, 0] = 0b11                                 # k=0 field = 3 (invalid)
-    p[1, 7] = 0b11000011                           # two invalid fields
+    p = np.full((2, 8), 0xFF, dtype=np.uint8)     # all fields 11 -> t = -1
+    p[0, 0] = 0b11111110                           # k=0 field = 10 (invalid)
+    p[1, 7] = 0b10111110                           # two invalid fields
     t, bad = oracle.unpack_ternary(p, 32)
     assert bad == 3
     assert t[0, 0] == 0 and t[0, 1] == -1
     assert set(np.unique(t)) <= {-1, 0}
+    p2 = np.array([[0b01000100, 0, 0, 0]], dtype=np.uint8)   # fields (k=0,2,4,6) = 00,01,00,01
+    t2, bad2 = oracle.unpack_ternary(p2, 16)
+    assert bad2 == 0 and list(t2[0, 0:8:2]) == [0, 1, 0, 1]
 
 
 def test_pack_rejects_out_of_set_codes():
