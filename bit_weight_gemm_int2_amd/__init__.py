@@ -101,6 +101,21 @@ def workspace_bytes(fmt, M: int, N: int, K: int) -> int:
     return int(lib().lowbit_gemm_workspace_bytes(_FMT[fmt], M, N, K))
 
 
+_WORKSPACES = {}
+
+
+def _shared_workspace(device: torch.device, nbytes: int) -> torch.Tensor:
+    """A workspace per device, reused by every call that passes none (calls
+    on one stream never overlap). It grows when a larger problem needs more;
+    grow it before any HIP graph capture by running the largest problem once."""
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    ws = _WORKSPACES.get(idx)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _WORKSPACES[idx] = ws
+    return ws
+
+
 def _pack(fn, codes: torch.Tensor, div: int, check: bool, stream) -> torch.Tensor:
     _cuda(codes, "codes")
     if codes.dtype != torch.int8 or codes.dim() != 2:
@@ -161,8 +176,11 @@ def gemm(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, fmt, bias:
     if out is None:
         out = torch.empty((M, N), dtype=odt, device=x.device)
     ws_need = workspace_bytes(fmt, M, N, K)
-    if ws_need and (workspace is None or workspace.numel() * workspace.element_size() < ws_need):
-        workspace = torch.empty(ws_need, dtype=torch.uint8, device=x.device)
+    if ws_need and workspace is None:
+        workspace = _shared_workspace(x.device, ws_need)
+    elif ws_need and workspace.numel() * workspace.element_size() < ws_need:
+        raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, "
+                         f"lowbit_gemm needs {ws_need}")
     st = lib().lowbit_gemm(
         _FMT[fmt], x.data_ptr(), _DT[x.dtype], M, K, x.stride(0),
         packed.data_ptr(), scales.data_ptr(), GROUP, N,

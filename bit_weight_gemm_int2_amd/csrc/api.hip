@@ -19,7 +19,7 @@ hipError_t launch_unpack(int fmt, const uint8_t* packed, int64_t N, int64_t K, i
 hipError_t launch_gemm(int fmt, bool x_bf16, GemmArgs a, int num_cu, int variant, hipStream_t st);
 hipError_t launch_gelu(const void* in, void* out, int dtype, int64_t count, hipStream_t st);
 size_t small_workspace_bytes(int M, int N, int K, int num_cu);
-int small_m_limit();
+bool small_path(int M, int N, int K, int variant);
 }  // namespace lowbit
 
 namespace {
@@ -145,9 +145,7 @@ size_t lowbit_gemm_workspace_bytes(int32_t format, int64_t M, int64_t N, int64_t
   if (M < 1 || N < 1 || K < 128 || K % 128 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return 0;
   int num_cu = 0;
   if (current_device(&num_cu)) return 0;
-  int variant = force_variant();
-  bool small = variant == 2 || (variant == 0 && M <= lowbit::small_m_limit());
-  if (!small || M > 16) return 0;
+  if (!lowbit::small_path((int)M, (int)N, (int)K, force_variant())) return 0;
   return lowbit::small_workspace_bytes((int)M, (int)N, (int)K, num_cu);
 }
 
@@ -194,8 +192,7 @@ int32_t lowbit_gemm(int32_t format, const void* X, int32_t x_dtype, int64_t M, i
   a.N = (int)N;
   a.K = (int)K;
   a.ws = (float*)workspace;
-  int variant = force_variant();
-  if (variant == 2 && M > 16) variant = 1;
+  const int variant = force_variant();
   hipError_t e = lowbit::launch_gemm(format == LOWBIT_TERNARY_INT2 ? lowbit::FMT_TERNARY : lowbit::FMT_BINARY,
                                      x_dtype == LOWBIT_BF16, a, num_cu, variant, (hipStream_t)stream);
   return e == hipSuccess ? LOWBIT_OK : LOWBIT_ERR_HIP;

@@ -41,12 +41,9 @@ __device__ __forceinline__ float bf16_bits_to_float(uint16_t h) {
   return __builtin_bit_cast(float, (uint32_t)h << 16);
 }
 
-// float -> bf16 bits, round to nearest even, NaN kept quiet.
+// float -> bf16 bits, round to nearest even (gfx950 v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 __device__ __forceinline__ uint16_t float_to_half_bits(float f) {
@@ -60,11 +57,24 @@ __device__ __forceinline__ float load_bias(const void* bias, int dtype, int n) {
   return 0.0f;
 }
 
-// x * Phi(x) with the exact error function, in FP32. Phi(x) is taken as
-// erfc(-x/sqrt2)/2, which keeps its relative accuracy for negative x where
-// 1 + erf(x/sqrt2) would cancel.
+// GELU with the error function, x * Phi(x), Phi(x) = (1 + erf(x / sqrt 2)) / 2.
+// erf is evaluated with the rational-exponential approximation of
+// Abramowitz & Stegun, Handbook of Mathematical Functions, eq. 7.1.26:
+//   erfc(z) ~ (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-z^2),
+//   t = 1 / (1 + p z), z >= 0, |error in erf| <= 1.5e-7.
+// For x < 0 Phi is taken directly as erfc(|x|/sqrt2)/2, so there is no
+// cancellation; the absolute error of GELU is below 1e-7 * |x| + a few FP32 ulps.
 __device__ __forceinline__ float gelu_erf(float x) {
-  return 0.5f * x * erfcf(-x * 0.70710678118654752440f);
+  const float z = fabsf(x) * 0.70710678118654752440f;
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(0.3275911f, z, 1.0f));
+  float poly = __builtin_fmaf(1.061405429f, t, -1.453152027f);
+  poly = __builtin_fmaf(poly, t, 1.421413741f);
+  poly = __builtin_fmaf(poly, t, -0.284496736f);
+  poly = __builtin_fmaf(poly, t, 0.254829592f);
+  poly *= t;
+  const float e = poly * __builtin_amdgcn_exp2f(-z * z * 1.44269504088896340736f);   // ~erfc(z)
+  const float phi = x >= 0.0f ? __builtin_fmaf(-0.5f, e, 1.0f) : 0.5f * e;
+  return x * phi;
 }
 
 __device__ __forceinline__ float finish(float acc, float b, int act) {

@@ -137,9 +137,9 @@ size_t lowbit_gemm_workspace_bytes(int32_t format, int64_t M, int64_t N, int64_t
  *   Y           [M][ldy] of y_dtype (F16, BF16, F32); aligned to its element
  *               size, ldy >= N; must not overlap X, W, scales, bias
  *   activation  LOWBIT_ACT_NONE or LOWBIT_ACT_GELU_ERF (x * Phi(x), exact erf)
- *   workspace   device scratch of at least lowbit_gemm_workspace_bytes();
- *               may be NULL when that is 0. Must not be shared by calls that
- *               can run concurrently.
+ *   workspace   device scratch of at least lowbit_gemm_workspace_bytes(),
+ *               16-byte aligned, any contents; may be NULL when that is 0.
+ *               Calls that can run concurrently must not share it.
  *   M, N, K     M, N >= 1; K >= 128 and K % 128 == 0; M, N, K < 2^31
  *
  * Ternary codes 10 are not checked here (hot path); they act as t = 0. The result is deterministic: the same

@@ -179,6 +179,35 @@ def test_small_and_large_kernels_agree_with_oracle(lb, force_variant, fmt, M, N,
         _assert_parity(Y, A, Mg, "bf16", f"{v} kernel")
 
 
+@pytest.mark.parametrize("fmt", ["ternary", "binary"])
+def test_split_k_is_deterministic_and_checks_workspace(lb, fmt):
+    """Split-K calls sum their partials in a fixed order: repeated calls give
+    identical bits, whatever the workspace held before."""
+    M, N, K = 16, 3072, 3072
+    need = lb.workspace_bytes(fmt, M, N, K)
+    assert need > 0                                   # this shape splits K
+    lin = wl.make_linear("split", fmt, M, N, K, seed=560, p0=0.35)
+    x = dev_bits(lin.x, "bf16")
+    packed, s = dev_weights(fmt, lin.codes, lin.scales)
+    ws = torch.full((need,), 0xAB, dtype=torch.uint8, device="cuda")
+    outs = [lb.gemm(x, packed, s, fmt, out_dtype=torch.float32, workspace=ws) for _ in range(3)]
+    torch.cuda.synchronize()
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int32), outs[0].view(torch.int32))
+    A, Mg = oracle_linear(lin)
+    _assert_parity(to_host64(outs[0]), A, Mg, "f32", "split-K")
+    with pytest.raises(ValueError):
+        lb.gemm(x, packed, s, fmt, workspace=ws[: need // 2])
+
+
+def test_very_long_k_small_m(lb):
+    """K beyond the small-M kernel's range (258 groups) takes the large-M path."""
+    lin = wl.make_linear("longk", "ternary", 2, 64, 258 * 128, seed=550, p0=0.35)
+    Y, _ = run_linear(lin)
+    A, Mg = oracle_linear(lin)
+    _assert_parity(Y, A, Mg, "bf16", "long K")
+
+
 @pytest.mark.parametrize("M", [4, 300])
 def test_deterministic_and_every_output_written(lb, M):
     lin = wl.make_linear("det", "ternary", M, 777, 1280, seed=600 + M, p0=0.35)
