@@ -170,6 +170,22 @@ def bench_small(torch, lb, reps=10):
     return out
 
 
+def traffic_probe(torch, lb):
+    """Workload for the rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE passes: first a
+    plain 256 MiB device copy (calibration: its byte counts are known), then two
+    passes of the MLP pair."""
+    a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+    bench_large(torch, lb, steps=1, warmup=1)
+    torch.cuda.synchronize()
+    print("traffic probe done", flush=True)
+
+
 def cpu_baseline(seconds_target=10.0):
     """The oracle as it stands (float64 dequantise + BLAS matmul) on a bounded
     sample of the step: the first R rows of the MLP pair (R grown up to all 4608),
@@ -211,6 +227,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-small", action="store_true")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="run the counter-calibration workload instead of the benchmark")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the low-bit linear layer runs on a single "
@@ -223,6 +241,9 @@ def main():
         print("no GPU available", file=sys.stderr)
         sys.exit(1)
     lb.lib()
+    if args.traffic_probe:
+        traffic_probe(torch, lb)
+        return
 
     r = bench_large(torch, lb, args.steps, args.warmup)
     ms_step = r["total_ms"] / args.steps
