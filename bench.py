@@ -35,10 +35,15 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_large_config3_traffic.json")
 
 
 def kernel_source_sha() -> str:
+    """Hash of the GEMM kernel source with comments and blank lines removed, so
+    that counter data stays attached to the code it was measured on."""
     h = hashlib.sha256()
     for f in ("gemm.hip", "common.h"):
-        with open(os.path.join(ROOT, "bit_weight_gemm_int2_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "bit_weight_gemm_int2_amd", "csrc", f)) as fh:
+            for line in fh:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 
@@ -232,7 +237,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the low-bit linear layer runs on a single "
-              "device here (see the sharding notes in DESIGN.md); run with --gpus 1", file=sys.stderr)
+              "device here; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -8,16 +8,18 @@
 // Both kernels compute, for every output element and every 128-group g,
 //   P_g = sum_{k in g} x_k * t_k            (MFMA, FP32 accumulation, exact
 //                                             products: t/2 is a power of two)
-//   acc += (2 s_g) * P_g                    (one FP32 FMA per group)
+//   acc += (2 s_g) * P_g                    (FP32; the large-M kernel does
+//                                             this in Horner form, below)
 // which is the definition up to FP32 rounding order. Zero, subnormal and
 // negative scales need no special case.
 //
-// MFMA: v_mfma_f32_16x16x32_{bf16,f16}. A lane l holds operand rows / output
-// columns l % 16 and K slots 8*(l/16) .. +7; the K order inside a 128-group is
-// free as long as both operands use the same one, so each lane group q = l/16
-// owns k-local [32q, 32q+32) of every group and chunk c (one MFMA) uses its
-// slots 32q + 8c .. +7. This lets a lane read its activations as 16 contiguous
-// bytes and its codes as one or two packed words.
+// MFMA: v_mfma_f32_32x32x16_{bf16,f16} in both kernels. Lane l supplies
+// operand row / output column l % 32 and K slots 8*(l/32) .. +7 of each MFMA.
+// The K order inside a 128-group is free as long as both operands use the same
+// one, so lane group q = l/32 owns k-local [64q, 64q+64) of every group and
+// MFMA step s (0..7) uses its slots 64q + 8s .. +7: a lane reads its
+// activations as 16 contiguous bytes per step and its codes for the whole
+// group as one 16-byte (ternary) or 8-byte (binary) load.
 #include "common.h"
 
 namespace lowbit {
