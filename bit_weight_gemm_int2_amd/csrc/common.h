@@ -93,89 +93,51 @@ __device__ __forceinline__ void store_out(void* Y, int64_t ldy, int dtype, int m
 // Code unpacking into MFMA operand registers.
 //
 // An MFMA operand register holds two 16-bit values. The kernels feed the MFMA
-// with t/2 (ternary) or -t/2 (binary) instead of t: both are exact in FP16 and
-// BF16 and their low byte is zero, so one byte lookup (ternary) or one
-// sign-bit insert (binary) builds a value. The factor 2 (or -2) is folded into
-// the group scale, where it is exact.
+// with 2t (ternary) or -2t (binary) instead of t. In both FP16 and BF16 the
+// value 2.0 is the single exponent bit 14, so +-2.0 is (bit 15 = sign,
+// bit 14 = 1) and 0 is all zeros; the factor 1/2 (or -1/2) is folded into the
+// group scale, where it is exact. Every value is then built by one rotate and
+// one mask (ternary) or one rotate and one AND-OR (binary), with no lookup.
 //
-// Ternary codes are the 2-bit two's complement of t (00 = 0, 01 = +1,
-// 11 = -1). After a right rotation the two codes of a register sit at bits
-// [9:8] and [25:24]; masking leaves a v_perm selector whose bytes 1 and 3 are
-// the codes and whose bytes 0 and 2 are zero. Byte 0 of the table is 0x00, so
-// the low bytes and t = 0 both read zero; bytes 1 and 3 hold the high bytes
-// of +0.5 and -0.5 (the invalid code 10 reads byte 2 = 0x00).
+// Ternary: the 2-bit two's complement code (bit 0: t != 0, bit 1: t < 0) is
+// bits 14..15 of 2t as they stand. Pair i of a packed word (its k = 2i and
+// 2i + 1) sits at bits 2i and 16 + 2i; rotating right by 18 + 2i (mod 32)
+// moves the pair to bits 14 and 30, and the mask 0xC000C000 leaves the two
+// values. The invalid code 10 becomes -0.0, i.e. t = 0.
+// Binary: pair i of a packed word (its k = 2i and 2i + 1) sits at bits i and
+// 16 + i; rotating right by 17 + i (mod 32) puts it on the two sign bits, and
+// OR-ing 2.0 into both halves gives -2t (bit 1 means t = +1).
 // ---------------------------------------------------------------------------
-template <bool BF16>
-__device__ __forceinline__ constexpr uint32_t tern_table() {
-  return BF16 ? 0xBF003F00u : 0xB8003800u;
+constexpr uint32_t TERN_MASK = 0xC000C000u;
+constexpr uint32_t BIN_SIGN = 0x80008000u, BIN_TWO = 0x40004000u;
+
+__device__ __forceinline__ uint32_t rotr(uint32_t w, int n) {
+  n &= 31;
+  return n ? __builtin_amdgcn_alignbit(w, w, (uint32_t)n) : w;
 }
 
-template <bool BF16>
-__device__ __forceinline__ uint32_t tern_pair(uint32_t w, uint32_t rot) {
-  uint32_t x = rot ? __builtin_amdgcn_alignbit(w, w, rot) : w;
-  return __builtin_amdgcn_perm(0u, tern_table<BF16>(), x & 0x03000300u);
-}
-
-// Variants with the table (ternary) or the sign mask and base (binary) passed
-// in registers, so a group whose scale is zero can use an all-zero table.
-__device__ __forceinline__ uint32_t tern_pair_t(uint32_t w, uint32_t rot, uint32_t table) {
-  uint32_t x = rot ? __builtin_amdgcn_alignbit(w, w, rot) : w;
-  return __builtin_amdgcn_perm(0u, table, x & 0x03000300u);
-}
-
-__device__ __forceinline__ u32x4 tern_chunk_t(uint32_t w, int c, uint32_t table) {
+// Eight consecutive k of a ternary word: pairs 4c .. 4c+3 (c = 0, 1);
+// register v holds pair 4c + v. A zero mask gives an all-zero operand.
+__device__ __forceinline__ u32x4 tern_chunk(uint32_t w, int c, uint32_t mask) {
   u32x4 r;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) r[v] = tern_pair_t(w, (uint32_t)((8 * (c & 1) + 2 * v + 24) & 31), table);
+  for (int v = 0; v < 4; ++v) r[v] = rotr(w, 18 + 2 * (4 * c + v)) & mask;
   return r;
 }
 
-__device__ __forceinline__ u32x4 bin_chunk_t(uint32_t w, int c, uint32_t mask, uint32_t base) {
+// Eight consecutive k of a binary word: pairs 4c .. 4c+3 (c = 0..3).
+// Zero sign mask and base give an all-zero operand.
+__device__ __forceinline__ u32x4 bin_chunk(uint32_t w, int c, uint32_t sign, uint32_t two) {
   u32x4 r;
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const uint32_t rot = (uint32_t)((4 * c + v + 17) & 31);
-    const uint32_t x = rot ? __builtin_amdgcn_alignbit(w, w, rot) : w;
-    r[v] = (x & mask) | base;
-  }
+  for (int v = 0; v < 4; ++v) r[v] = (rotr(w, 17 + 4 * c + v) & sign) | two;
   return r;
 }
 
-// Binary: after a right rotation the two bits of a register sit at bits 15
-// and 31, i.e. on the sign bits of the two halves of +0.5; bit 1 (t = +1)
-// gives -0.5 = -t/2.
-template <bool BF16>
-__device__ __forceinline__ uint32_t bin_pair(uint32_t w, uint32_t rot) {
-  uint32_t x = rot ? __builtin_amdgcn_alignbit(w, w, rot) : w;
-  return (x & 0x80008000u) | (BF16 ? 0x3F003F00u : 0x38003800u);
-}
-
-// Operand registers for chunk c (c = 0..3) of one 128-group, for the lane
-// group that owns k-local [32q, 32q+32) of the group. Slot s of the chunk is
-// k-local 32q + 8c + s; register v holds slots 2v (low half) and 2v+1.
-//
-// Ternary: the lane group's 32 codes are words w0 (k-local 32q..32q+15) and
-// w1 (32q+16..32q+31). k-local 32q + 8c + 2v + h lives in word c/2 at bit
-// 16h + 2(4(c%2) + v); rotating right by 8(c%2) + 2v - 8 (mod 32) puts the
-// pair at bits 8 and 24.
-template <bool BF16>
-__device__ __forceinline__ u32x4 tern_chunk(uint32_t w0, uint32_t w1, int c) {
-  uint32_t w = (c < 2) ? w0 : w1;
-  u32x4 r;
-#pragma unroll
-  for (int v = 0; v < 4; ++v) r[v] = tern_pair<BF16>(w, (uint32_t)((8 * (c & 1) + 2 * v + 24) & 31));
-  return r;
-}
-
-// Binary: the lane group's 32 bits are one word w; k-local 32q + 8c + 2v + h
-// is bit 16h + 4c + v; rotating right by 4c + v + 17 (mod 32) puts the pair
-// at bits 15 and 31.
-template <bool BF16>
-__device__ __forceinline__ u32x4 bin_chunk(uint32_t w, int c) {
-  u32x4 r;
-#pragma unroll
-  for (int v = 0; v < 4; ++v) r[v] = bin_pair<BF16>(w, (uint32_t)((4 * c + v + 17) & 31));
-  return r;
+// Factor that turns an MFMA sum of the fed values back into sum x * t.
+template <bool TERN>
+__device__ __forceinline__ constexpr float code_factor() {
+  return TERN ? 0.5f : -0.5f;
 }
 
 template <bool BF16>
@@ -188,14 +150,5 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
-template <bool BF16>
-__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
-  if constexpr (BF16)
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-  else
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
-                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-}
 
 }  // namespace lowbit

@@ -6,9 +6,9 @@
 // t stored with 2 bits (ternary) or 1 bit (binary).
 //
 // Both kernels compute, for every output element and every 128-group g,
-//   P_g = sum_{k in g} x_k * t_k            (MFMA, FP32 accumulation, exact
-//                                             products: t/2 is a power of two)
-//   acc += (2 s_g) * P_g                    (FP32; the large-M kernel does
+//   P_g = sum_{k in g} x_k * (2 t_k)        (MFMA, FP32 accumulation, exact
+//                                             products: 2t is 0 or +-2)
+//   acc += (s_g / 2) * P_g                  (FP32; the large-M kernel does
 //                                             this in Horner form, below)
 // which is the definition up to FP32 rounding order. Zero, subnormal and
 // negative scales need no special case.
@@ -41,7 +41,7 @@ namespace lowbit {
 //    ahead of use. A lane loads 16 bytes (ternary) or 8 bytes (binary): the
 //    64 codes its lane group contributes to the group.
 //  * Group scales, Horner form: the MFMAs accumulate in units of the current
-//    group's scale c_g = +-2 s_g, and at each group boundary the accumulator
+//    group's scale c_g = +-s_g / 2, and at each group boundary the accumulator
 //    is rescaled by c_{g-1} / c_g (one FP32 multiply per element); after the
 //    last group it is multiplied by c_G. In exact arithmetic this is
 //    sum_g c_g P_g; in FP32 each rescale adds one rounding (about 2G ulps of
@@ -80,9 +80,7 @@ __global__ __launch_bounds__(256, 1) void gemm_large_kernel(GemmArgs a, int tile
   const int m0 = (t / tiles_n) * BM, n0 = (t % tiles_n) * BN;
   const int G = a.K >> 7;
   const int64_t wrow = TERN ? (a.K >> 2) : (a.K >> 3);
-  const float factor = TERN ? 2.0f : -2.0f;
-  const uint32_t table = tern_table<BF16>();
-  const uint32_t bmask = 0x80008000u, bbase = BF16 ? 0x3F003F00u : 0x38003800u;
+  const float factor = code_factor<TERN>();
 
   // ---- activation stage g -> LDS buffer `buf` (wave w: rows 32w .. 32w+31) ----
   auto dma = [&](int g, int buf) {
@@ -137,14 +135,14 @@ __global__ __launch_bounds__(256, 1) void gemm_large_kernel(GemmArgs a, int tile
     const bool zero = s == 0.0f;
     const float r = zero ? 1.0f : cref[j] / s;
     cref[j] = zero ? cref[j] : s;
-    const uint32_t tb = zero ? 0u : table;
-    const uint32_t mk = zero ? 0u : bmask, bs = zero ? 0u : bbase;
+    const uint32_t tm = zero ? 0u : TERN_MASK;
+    const uint32_t mk = zero ? 0u : BIN_SIGN, bs = zero ? 0u : BIN_TWO;
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i][j] *= r;
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
-      const u32x4 bf = TERN ? tern_chunk_t(bw[j][st >> 1], st & 1, tb)
-                            : bin_chunk_t(bw[j][st >> 2], st & 3, mk, bs);
+      const u32x4 bf = TERN ? tern_chunk(bw[j][st >> 1], st & 1, tm)
+                            : bin_chunk(bw[j][st >> 2], st & 3, mk, bs);
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i][j] = mfma32<BF16>(A[i][st], bf, acc[i][j]);
       if (refill) {
@@ -268,7 +266,7 @@ __global__ __launch_bounds__(256, 1) void gemm_large_kernel(GemmArgs a, int tile
 //  2. Each wave issues the code loads of its whole range (16 bytes per lane
 //     per group, the lane-group K order of the large-M kernel) and the raw
 //     scales before its first MFMA: one memory latency covers the kernel.
-//  3. Per group: tmp = 8 MFMAs, part += (+-2 s) * tmp on the accumulator
+//  3. Per group: tmp = 8 MFMAs, part += (+-s / 2) * tmp on the accumulator
 //     registers that hold real rows (8 of 16).
 // With a.splits > 1 the group range is split across workgroups and FP32
 // partials go to the workspace, summed afterwards in split order
@@ -292,7 +290,7 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a) {
   const int lane = tid & 63, q = lane >> 5, r32 = lane & 31;
   const int G = a.K >> 7;
   const int64_t wrow = TERN ? (a.K >> 2) : (a.K >> 3);
-  const float factor = TERN ? 2.0f : -2.0f;
+  const float factor = code_factor<TERN>();
   const int g0 = blockIdx.y * a.gps;
   const int ng = min(G - g0, a.gps);                    // 1 .. GMAX
   const int n = blockIdx.x * 128 + wave * 32 + r32;
@@ -354,9 +352,8 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a) {
         for (int u = 0; u < 4; ++u) {
           const int i = i0 + u;
           const u32x4 af = sX[((i * 2 + q) * 8 + st) * XROWS + xr];
-          const u32x4 bf = TERN ? tern_chunk_t(wd[i][st >> 1], st & 1, tern_table<BF16>())
-                                : bin_chunk_t(wd[i][st >> 2], st & 3, 0x80008000u,
-                                              BF16 ? 0x3F003F00u : 0x38003800u);
+          const u32x4 bf = TERN ? tern_chunk(wd[i][st >> 1], st & 1, TERN_MASK)
+                                : bin_chunk(wd[i][st >> 2], st & 3, BIN_SIGN, BIN_TWO);
           tmp[u] = mfma32<BF16>(af, bf, st == 0 ? f32x16{} : tmp[u]);
         }
       }
