@@ -141,7 +141,7 @@ def bench_small(torch, lb, reps=10):
                   for K in sorted({K for _, _, K in shapes})}
             ys = [torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for _, _, N, _ in layers]
             need = max(lb.workspace_bytes(fmt, M, N, K) for _, _, N, K in layers)
-            ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+            ws = lb.new_workspace(need)
 
             def sweep():
                 for (p, s, N, K), yy in zip(layers, ys):

@@ -104,6 +104,12 @@ def workspace_bytes(fmt, M: int, N: int, K: int) -> int:
 _WORKSPACES = {}
 
 
+def new_workspace(nbytes: int, device=None) -> torch.Tensor:
+    """A workspace for lowbit_gemm: zeroed device bytes (the library returns
+    its counters to zero after every call, so it stays reusable)."""
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device or "cuda")
+
+
 def _shared_workspace(device: torch.device, nbytes: int) -> torch.Tensor:
     """A workspace per device, reused by every call that passes none (calls
     on one stream never overlap). It grows when a larger problem needs more;
@@ -111,7 +117,7 @@ def _shared_workspace(device: torch.device, nbytes: int) -> torch.Tensor:
     idx = device.index if device.index is not None else torch.cuda.current_device()
     ws = _WORKSPACES.get(idx)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        ws = new_workspace(max(nbytes, 1 << 20), device)
         _WORKSPACES[idx] = ws
     return ws
 

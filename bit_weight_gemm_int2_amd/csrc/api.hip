@@ -175,7 +175,7 @@ int32_t lowbit_gemm(int32_t format, const void* X, int32_t x_dtype, int64_t M, i
   if (st) return st;
   size_t need = lowbit_gemm_workspace_bytes(format, M, N, K);
   if (need && (!workspace || workspace_bytes < need)) return LOWBIT_ERR_WORKSPACE;
-  if (need && !aligned(workspace, 16)) return LOWBIT_ERR_ALIGN;
+  if (need && !aligned(workspace, 256)) return LOWBIT_ERR_ALIGN;
 
   lowbit::GemmArgs a{};
   a.X = (const uint16_t*)X;

@@ -7,6 +7,7 @@ namespace lowbit {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -28,9 +29,7 @@ struct GemmArgs {
   int y_dtype;
   int act;
   int M, N, K;
-  float* ws;           // split-K partials [splits][M][N] (small-M path only)
-  int splits;          // number of K slices
-  int gps;             // 128-groups per K slice
+  float* ws;           // caller workspace (no kernel uses one at present)
 };
 
 __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
@@ -138,6 +137,16 @@ __device__ __forceinline__ u32x4 bin_chunk(uint32_t w, int c, uint32_t sign, uin
 template <bool TERN>
 __device__ __forceinline__ constexpr float code_factor() {
   return TERN ? 0.5f : -0.5f;
+}
+
+template <bool BF16>
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (BF16)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
 template <bool BF16>

@@ -257,160 +257,214 @@ __global__ __launch_bounds__(256, 1) void gemm_large_kernel(GemmArgs a, int tile
 }
 
 // ===========================================================================
-// Small-M kernel (M <= 16): weight streaming with v_mfma_f32_32x32x16 (rows
-// 16..31 of every MFMA are padding). A workgroup owns 4 column blocks of 32
-// (one per wave) and a range of at most GMAX 128-groups.
-//  1. The activations of that K range (M rows, zero rows up to 16) are staged
-//     once in LDS, laid out so that an MFMA fragment read (16 lanes, 16 bytes
-//     each) is one contiguous, conflict-free 256-byte block.
-//  2. Each wave issues the code loads of its whole range (16 bytes per lane
-//     per group, the lane-group K order of the large-M kernel) and the raw
-//     scales before its first MFMA: one memory latency covers the kernel.
-//  3. Per group: tmp = 8 MFMAs, part += (+-s / 2) * tmp on the accumulator
-//     registers that hold real rows (8 of 16).
-// With a.splits > 1 the group range is split across workgroups and FP32
-// partials go to the workspace, summed afterwards in split order
-// (deterministic).
+// Small-M kernel (M <= 16): weight streaming with v_mfma_f32_16x16x32.
+// The grid is (column tiles) x (K splits). A workgroup of WC waves owns a
+// tile of 16 WC output columns (16 per wave) and one slice of at most GS
+// 128-groups of K:
+//  * The activations of the slice (rows >= M repeat row M - 1: MFMA rows are
+//    independent and those outputs are never stored) go global -> LDS once
+//    per workgroup with direct LDS DMA loads, each instruction reading four
+//    whole 256-byte group rows; 16-byte chunks are XOR-swizzled by row, which
+//    makes the MFMA fragment reads conflict-free.
+//  * Codes: every lane issues 16-byte loads that cover two groups of its
+//    column (ternary: the four lane groups read 64 contiguous bytes of the
+//    column) or one group (binary: 16 bytes = 128 codes), so a wave-wide
+//    instruction reads 64 contiguous bytes per column. v_permlane32_swap
+//    (and v_permlane16_swap for binary) then hands every lane its own share
+//    of each group. All loads of the slice are issued before one wait.
+//  * MFMA rows are output rows, MFMA columns are output columns; each group
+//    is four chained MFMAs, then acc += (scale * factor) * tmp in FP32. Four
+//    groups are interleaved (four independent chains); slots past the slice
+//    up to the next multiple of four hold zeros and a zero scale.
+//  * K order inside a group (both operands): binary lane group q takes
+//    k-local [32q, 32q+32) in steps of 8; ternary lane group q takes
+//    b + {0..15} and b + {32..47} with b = {0, 64, 16, 80}[q], which is what
+//    the lane exchange leaves in its registers.
+//  * With one split the result is stored directly. Otherwise every workgroup
+//    writes its FP32 partial tile with agent-scope stores, waits for them,
+//    and takes a ticket for its column tile (agent-scope atomic add); the
+//    workgroup that takes the last ticket reads the partials back with
+//    agent-scope loads, sums them in split order (deterministic), applies
+//    bias and activation, stores Y and resets the ticket to zero. Only
+//    atomic-scope accesses touch the partials and tickets, so no L2
+//    writeback or invalidate is needed.
 // ===========================================================================
-constexpr int MAX_SPLITS = 16;           // K splits of the small-M kernel
+namespace stream {
+constexpr int MAXGS = 32;                      // groups per workgroup slice
+constexpr int MAXSPLIT = 16;                   // K splits
+__host__ __device__ constexpr size_t lds_bytes(int gs) { return (size_t)gs * 16 * 256; }
+// workspace: one 32-bit ticket per column tile in a fixed region at the
+// start (so calls of any shape reuse the same, zero, counters), then the FP32
+// partials [splits][M][N]
+constexpr int MAXTILES = 16384;
+constexpr size_t TICKET_BYTES = (size_t)MAXTILES * 4;
+}  // namespace stream
 
-namespace small {
-constexpr int GMAX = 16;                 // groups per workgroup (register budget)
-constexpr int XROWS = 16;
-}  // namespace small
+template <bool TERN>
+__device__ __forceinline__ int stream_chunk(int q, int s) {
+  // 8-k chunk of the group row used by lane group q at MFMA step s
+  return TERN ? ((q & 1) * 8 + (q >> 1) * 2 + (s & 1) + (s >> 1) * 4) : (4 * q + s);
+}
 
-template <bool BF16, int FMT>
-__global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a) {
-  using namespace small;
+template <bool BF16, int FMT, int WC, int GS>
+__global__ __launch_bounds__(64 * WC) void gemm_stream_kernel(GemmArgs a, int splits, int gps) {
   constexpr bool TERN = FMT == FMT_TERNARY;
-  // [group][lane group q][step][row] of 16-byte activation chunks
-  __shared__ u32x4 sX[GMAX * 2 * 8 * XROWS];
-  const int tid = threadIdx.x;
+  constexpr int NW = TERN ? GS / 2 : GS / 4;          // 16-byte code loads per lane
+  extern __shared__ __align__(16) uint8_t smem[];      // [GS][16 rows][256 B] activations
+  __shared__ int last_flag;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63, q = lane >> 5, r32 = lane & 31;
+  const int q = lane >> 4, c16 = lane & 15;
   const int G = a.K >> 7;
+  const int tile = blockIdx.x, split = blockIdx.y;
+  const int g0 = split * gps;
+  const int ng = min(gps, G - g0);                      // 1 .. GS (host plan)
+  const int n = (tile * WC + wave) * 16 + c16;
+  const int64_t nc = min(n, a.N - 1);                   // clamped: loads stay in bounds
   const int64_t wrow = TERN ? (a.K >> 2) : (a.K >> 3);
   const float factor = code_factor<TERN>();
-  const int g0 = blockIdx.y * a.gps;
-  const int ng = min(G - g0, a.gps);                    // 1 .. GMAX
-  const int n = blockIdx.x * 128 + wave * 32 + r32;
-  const int nc = min(n, a.N - 1);                       // clamped: loads stay in bounds
 
-  // (1) activations of the range: every load is issued before any LDS write
-  // (a loop that waited on each load would pay one memory latency per group).
-  // Thread t covers row t/16, 16-byte chunk t%16 of each group (coalesced);
-  // rows >= M and the padding groups up to the next multiple of four are
-  // zero, so every fragment read below is unconditional.
-  const int ng4 = (ng + 3) & ~3;
-  u32x4 xs[GMAX];
-  {
-    const int row = tid >> 4, ch = tid & 15;
+  // (1) activations of the slice -> LDS: instruction t of this wave covers
+  // rows 4j .. 4j+3 of group i (slot i of the tile)
 #pragma unroll
-    for (int i = 0; i < GMAX; ++i) {
-      xs[i] = u32x4{0u, 0u, 0u, 0u};
-      if (i < ng && row < a.M) xs[i] = *(const u32x4*)(a.X + (int64_t)row * a.ldx + ((g0 + i) << 7) + 8 * ch);
+  for (int t = 0; t < 4 * GS / WC; ++t) {
+    const int idx = t * WC + wave;
+    const int i = idx >> 2, j = idx & 3;
+    if (i < ng) {                                       // wave-uniform
+      const int r = 4 * j + q;                          // tile row of this lane
+      const uint16_t* src = a.X + (int64_t)min(r, a.M - 1) * a.ldx + ((g0 + i) << 7) + 8 * ((c16 ^ r) & 15);
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr_t)(smem + i * 4096 + j * 1024), 16, 0, 0);
     }
   }
-  // (2) codes and scales of the whole range, in flight during the staging
-  u32x4 wd[GMAX];
-  uint16_t sb[GMAX];
-  const uint8_t* wp = a.W + (int64_t)nc * wrow;
+  // slots past the slice up to the next multiple of 4 are computed with zero
+  // activations (and a zero scale), so they add exactly zero
+  {
+    const int zend = min(GS, (ng + 3) & ~3);
+    for (int z = ng * 256 + tid; z < zend * 256; z += 64 * WC)
+      *(u32x4*)(smem + (size_t)z * 16) = u32x4{0u, 0u, 0u, 0u};
+  }
+  // (2) codes: ternary load p covers groups 2p (lane groups 0, 1) and 2p+1
+  // (lane groups 2, 3); binary load p: lane group q reads group 4p + q
+  const uint8_t* wp = a.W + nc * wrow;
+  u32x4 cw[NW];
 #pragma unroll
-  for (int i = 0; i < GMAX; ++i) {
-    const int g = g0 + min(i, ng - 1);
+  for (int p = 0; p < NW; ++p) {
     if (TERN) {
-      wd[i] = *(const u32x4*)(wp + g * 32 + 16 * q);
+      const int g = g0 + min(2 * p + (q >> 1), ng - 1);
+      cw[p] = *(const u32x4*)(wp + g * 32 + 16 * (q & 1));
     } else {
-      const u32x2 v = *(const u32x2*)(wp + g * 16 + 8 * q);
-      wd[i] = u32x4{v[0], v[1], 0u, 0u};
+      const int g = g0 + min(4 * p + q, ng - 1);
+      cw[p] = *(const u32x4*)(wp + g * 16);
     }
-    sb[i] = a.S[(int64_t)nc * G + g];
+  }
+  // (3) raw scales: lane group q holds groups 4j + q of its column
+  uint32_t sr[GS / 4];
+#pragma unroll
+  for (int j = 0; j < GS / 4; ++j) sr[j] = a.S[nc * G + g0 + min(4 * j + q, ng - 1)];
+  __builtin_amdgcn_s_waitcnt(0);                        // this wave's loads and LDS DMA
+  __syncthreads();                                      // everyone's LDS DMA
+
+  // (4) lane exchange: afterwards ternary group 2p is in (cw[p][0], cw[p][2])
+  // and group 2p+1 in (cw[p][1], cw[p][3]); binary group 4p+j is cw[p][j]
+#pragma unroll
+  for (int p = 0; p < NW; ++p) {
+    if (TERN) {
+      auto x = __builtin_amdgcn_permlane32_swap(cw[p][0], cw[p][1], false, false);
+      auto y = __builtin_amdgcn_permlane32_swap(cw[p][2], cw[p][3], false, false);
+      cw[p] = u32x4{x[0], x[1], y[0], y[1]};
+    } else {
+      auto x = __builtin_amdgcn_permlane32_swap(cw[p][0], cw[p][2], false, false);
+      auto y = __builtin_amdgcn_permlane32_swap(cw[p][1], cw[p][3], false, false);
+      auto u = __builtin_amdgcn_permlane16_swap(x[0], y[0], false, false);
+      auto v = __builtin_amdgcn_permlane16_swap(x[1], y[1], false, false);
+      cw[p] = u32x4{u[0], u[1], v[0], v[1]};
+    }
   }
 
-  {
-    const int row = tid >> 4, ch = tid & 15;          // chunk ch = 8 * qq + st
+  // (5) MFMAs, four groups at a time: four independent chains, no branch
+  // inside a block (groups past the slice read zero activations)
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-    for (int i = 0; i < GMAX; ++i)
-      if (i < ng4) sX[(i * 16 + ch) * XROWS + row] = xs[i];
-  }
-  __syncthreads();
-
-  // (3) MFMAs: four groups at a time, so four independent accumulation
-  // chains are interleaved (one chain alone would wait out the MFMA latency)
-  float part[8];
-#pragma unroll
-  for (int r = 0; r < 8; ++r) part[r] = 0.0f;
-  // lanes 16..31 read row r32 - 16 again: MFMA rows 16..31 are never used
-  const int xr = r32 & (XROWS - 1);
-#pragma unroll
-  for (int i0 = 0; i0 < GMAX; i0 += 4) {
-    if (i0 < ng) {
-      f32x16 tmp[4];
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int i = i0 + u;
-          const u32x4 af = sX[((i * 2 + q) * 8 + st) * XROWS + xr];
-          const u32x4 bf = TERN ? tern_chunk(wd[i][st >> 1], st & 1, TERN_MASK)
-                                : bin_chunk(wd[i][st >> 2], st & 3, BIN_SIGN, BIN_TWO);
-          tmp[u] = mfma32<BF16>(af, bf, st == 0 ? f32x16{} : tmp[u]);
-        }
-      }
+  for (int bk = 0; bk < GS / 4; ++bk) {
+    if (4 * bk < ng) {                                  // wave-uniform
+      float sc[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        // padding groups multiply zero activations; their scale is not used
-        const float sc = (i0 + u < ng) ? factor * half_bits_to_float(sb[i0 + u]) : 0.0f;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) part[r] += sc * tmp[u][r];
+        const int sbits = __shfl((int)sr[bk], 16 * u + c16);
+        sc[u] = 4 * bk + u < ng ? factor * half_bits_to_float((uint16_t)sbits) : 0.0f;
       }
+      f32x4 tmp[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int i = 4 * bk + u;
+          const u32x4 af = *(const u32x4*)(smem + i * 4096 + c16 * 256 + ((stream_chunk<TERN>(q, s) ^ c16) << 4));
+          u32x4 bf;
+          if (TERN) bf = tern_chunk(cw[i >> 1][(i & 1) + 2 * (s >> 1)], s & 1, TERN_MASK);
+          else bf = bin_chunk(cw[i >> 2][i & 3], s, BIN_SIGN, BIN_TWO);
+          tmp[u] = mfma16<BF16>(af, bf, s == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : tmp[u]);
+        }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc += sc[u] * tmp[u];
     }
   }
 
-  // registers r < 8 hold rows 8*(r/4) + 4q + (r%4) < 16 of column n
-  if (a.splits == 1) {
-    if (n < a.N) {
+  // (6) output: lane holds rows 4q + e (e = 0..3) of column n
+  const bool col_ok = n < a.N;
+  if (splits == 1) {
+    if (col_ok) {
       const float b = a.bias ? load_bias(a.bias, a.bias_dtype, n) : 0.0f;
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int m = 8 * (r >> 2) + 4 * q + (r & 3);
-        if (m < a.M) store_out(a.Y, a.ldy, a.y_dtype, m, n, finish(part[r], b, a.act));
-      }
+      for (int e = 0; e < 4; ++e)
+        if (4 * q + e < a.M) store_out(a.Y, a.ldy, a.y_dtype, 4 * q + e, n, finish(acc[e], b, a.act));
     }
     return;
   }
-  // split K: FP32 partials, summed by splitk_reduce_kernel in split order
-  if (n < a.N) {
-    const int64_t MN = (int64_t)a.M * a.N;
+  // partial tiles, lane-major: [split][tile][wave][lane] x 4 floats, written
+  // and read as two 64-bit agent-scope atomics per lane
+  int* ticket = (int*)a.ws + tile;
+  uint64_t* part = (uint64_t*)((uint8_t*)a.ws + stream::TICKET_BYTES);
+  const int64_t tile_lanes = (int64_t)gridDim.x * WC * 64;
+  const int64_t my = (int64_t)(tile * WC + wave) * 64 + lane;
+  {
+    uint64_t* dst = part + 2 * ((int64_t)split * tile_lanes + my);
+    __hip_atomic_store(dst, __builtin_bit_cast(uint64_t, f32x2{acc[0], acc[1]}), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(dst + 1, __builtin_bit_cast(uint64_t, f32x2{acc[2], acc[3]}), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);                        // partial stores complete
+  __syncthreads();
+  if (tid == 0)
+    last_flag = __hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == splits - 1;
+  __syncthreads();
+  if (!last_flag) return;
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  // all partial loads in flight at once, then the sum in split order
+  uint64_t pv[stream::MAXSPLIT][2];
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int m = 8 * (r >> 2) + 4 * q + (r & 3);
-      if (m < a.M) a.ws[blockIdx.y * MN + (int64_t)m * a.N + n] = part[r];
+  for (int t = 0; t < stream::MAXSPLIT; ++t) {
+    const uint64_t* src = part + 2 * ((int64_t)min(t, splits - 1) * tile_lanes + my);
+    pv[t][0] = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    pv[t][1] = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int t = 0; t < stream::MAXSPLIT; ++t) {
+    if (t < splits) {
+      const f32x2 lo = __builtin_bit_cast(f32x2, pv[t][0]), hi = __builtin_bit_cast(f32x2, pv[t][1]);
+      sum += f32x4{lo[0], lo[1], hi[0], hi[1]};
     }
   }
-}
-
-// Sum of split-K partials in split order, then bias, activation and cast.
-// The split loop is unrolled to a fixed bound so all partial loads of an
-// element are in flight together (a rolled loop would wait once per split).
-// A separate launch: completing the sum inside the GEMM would need a
-// device-scope fence per workgroup, which on this multi-XCD part (one L2 per
-// XCD) costs far more than the extra launch.
-__global__ void splitk_reduce_kernel(GemmArgs a) {
-  const int64_t total = (int64_t)a.M * a.N;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    float p[MAX_SPLITS];
-#pragma unroll
-    for (int s = 0; s < MAX_SPLITS; ++s) p[s] = s < a.splits ? a.ws[(int64_t)s * total + i] : 0.0f;
-    float v = p[0];
-#pragma unroll
-    for (int s = 1; s < MAX_SPLITS; ++s)
-      if (s < a.splits) v += p[s];
-    const int m = (int)(i / a.N), n = (int)(i % a.N);
+  if (col_ok) {
     const float b = a.bias ? load_bias(a.bias, a.bias_dtype, n) : 0.0f;
-    store_out(a.Y, a.ldy, a.y_dtype, m, n, finish(v, b, a.act));
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (4 * q + e < a.M) store_out(a.Y, a.ldy, a.y_dtype, 4 * q + e, n, finish(sum[e], b, a.act));
   }
+  if (tid == 0) __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Standalone exact-erf GELU.
@@ -432,59 +486,81 @@ __global__ void gelu_kernel(const void* in, void* out, int dtype, int64_t count)
 // Host-side launch helpers
 // ===========================================================================
 
-// Small-M plan: column tiles of 128 (4 waves x 32) and a K split into ranges
-// of at most small::GMAX groups; split further (down to 2 groups per range)
-// while there are fewer than one workgroup per CU.
-struct SmallPlan { int splits, gps; };
+// Small-M plan: tiles of 64 columns (4 waves), or 128 (8 waves) when that
+// still gives at least 128 tiles; then the K split S (1 .. MAXSPLIT, at most
+// MAXGS groups per slice) that minimises a rough time estimate:
+//   rounds * (slice bytes through one CU at ~64 B/clk + slice MFMA work)
+//   + a fixed cost for the cross-workgroup combine when S > 1
+// (the combine waits for written partials, a ticket and the read-back, each
+// a memory round trip). The compiled slice size GS is gps rounded up to a
+// multiple of 4 (8 from 16 on).
+struct StreamPlan { int wc, gs, gps, splits, tiles; };
 
-static SmallPlan small_plan(int M, int N, int K, int num_cu) {
-  (void)M;
+static int round_gs(int g) { return g <= 4 ? 4 : g <= 8 ? 8 : g <= 12 ? 12 : g <= 16 ? 16 : g <= 24 ? 24 : 32; }
+
+static bool stream_plan(int M, int N, int K, int num_cu, StreamPlan* out) {
+  if (M > 16) return false;
   const int G = K / 128;
-  const int tiles = (N + 127) / 128;
-  // candidates: every split count from the minimum (ranges of <= GMAX groups)
-  // up to MAX_SPLITS with at least 2 groups per range; score = rounds of
-  // workgroups over the CUs (2 resident per CU) weighted by the work of one
-  // workgroup, plus the cost of writing and re-reading the partials
-  const int smin = (G + small::GMAX - 1) / small::GMAX;
-  SmallPlan best{1, G};
-  double best_cost = 1e30;
-  for (int sp = smin; sp <= MAX_SPLITS; ++sp) {
+  const int t8 = (N + 127) / 128, t4 = (N + 63) / 64;
+  const int wc = t8 >= 128 ? 8 : 4;
+  const int tiles = wc == 8 ? t8 : t4;
+  if (tiles > stream::MAXTILES || G > stream::MAXGS * stream::MAXSPLIT) return false;
+  double best = 1e30;
+  StreamPlan bp{};
+  for (int sp = 1; sp <= min(stream::MAXSPLIT, G); ++sp) {
     const int gps = (G + sp - 1) / sp;
-    if (gps > small::GMAX || (sp > smin && gps < 2)) continue;
-    const int splits = (G + gps - 1) / gps;
-    const int wgs = tiles * splits;
-    const int rounds = (wgs + 2 * num_cu - 1) / (2 * num_cu);
-    // one round costs about a memory latency plus its group count
-    double cost = rounds * (8.0 + gps);
-    if (splits > 1) cost += 6.0 + 0.05 * splits;   // reduce launch + partial traffic
-    if (wgs < num_cu) cost += 4.0 * (num_cu - wgs) / num_cu;   // idle CUs
-    if (cost < best_cost) {
-      best_cost = cost;
-      best.splits = splits;
-      best.gps = gps;
+    if (gps > stream::MAXGS) continue;
+    const int S = (G + gps - 1) / gps;
+    const int gs = round_gs(gps);
+    const size_t lds = stream::lds_bytes(gs);
+    const int per_cu = max(1, min((int)(160 * 1024 / lds), 32 / wc));
+    const int rounds = (tiles * S + num_cu * per_cu - 1) / (num_cu * per_cu);
+    const double clk = gps * (4096.0 + wc * 16 * 32) / 64.0 + gps * 4 * 40.0;
+    const double us = rounds * clk / 2100.0 + (S > 1 ? 3.0 : 0.0);
+    if (us < best) {
+      best = us;
+      bp = StreamPlan{wc, gs, gps, S, tiles};
     }
   }
-  return best;
+  *out = bp;
+  return best < 1e29;
 }
 
-// The small-M kernel covers K up to GMAX * MAX_SPLITS groups; beyond that
-// (K > 32768) the large-M kernel runs instead.
+// The small-M kernel covers every M <= 16 with N <= 16384 * 128 (unless the
+// large-M kernel is forced).
 bool small_path(int M, int N, int K, int variant) {
-  (void)N;
-  if (M > 16 || K / 128 > small::GMAX * MAX_SPLITS) return false;
-  return variant == 2 || (variant == 0 && M <= 16);
+  if (variant == 1) return false;
+  StreamPlan p;
+  return stream_plan(M, N, K, 256, &p);
 }
 
-// Workspace: FP32 partials [splits][M][N].
+// Workspace of the small-M kernel when K is split: partials and tickets.
 size_t small_workspace_bytes(int M, int N, int K, int num_cu) {
-  SmallPlan p = small_plan(M, N, K, num_cu);
-  return p.splits > 1 ? (size_t)p.splits * M * N * sizeof(float) : 0;
+  StreamPlan p;
+  if (!stream_plan(M, N, K, num_cu, &p) || p.splits == 1) return 0;
+  return stream::TICKET_BYTES + (size_t)p.splits * p.tiles * p.wc * 64 * 4 * sizeof(float);
 }
 
 template <bool BF16, int FMT>
-static void launch_small_t(GemmArgs& a, const SmallPlan& p, hipStream_t st) {
-  dim3 grid((a.N + 127) / 128, p.splits);
-  hipLaunchKernelGGL((gemm_small_kernel<BF16, FMT>), grid, dim3(256), 0, st, a);
+static void launch_stream_t(const GemmArgs& a, const StreamPlan& p, hipStream_t st) {
+  const dim3 grid(p.tiles, p.splits), block(64 * p.wc);
+  const size_t lds = stream::lds_bytes(p.gs);
+#define LOWBIT_STREAM(WC, GS) \
+  hipLaunchKernelGGL((gemm_stream_kernel<BF16, FMT, WC, GS>), grid, block, lds, st, a, p.splits, p.gps)
+#define LOWBIT_STREAM_GS(WC)             \
+  if (p.gs == 4) LOWBIT_STREAM(WC, 4);   \
+  else if (p.gs == 8) LOWBIT_STREAM(WC, 8);   \
+  else if (p.gs == 12) LOWBIT_STREAM(WC, 12); \
+  else if (p.gs == 16) LOWBIT_STREAM(WC, 16); \
+  else if (p.gs == 24) LOWBIT_STREAM(WC, 24); \
+  else LOWBIT_STREAM(WC, 32);
+  if (p.wc == 8) {
+    LOWBIT_STREAM_GS(8)
+  } else {
+    LOWBIT_STREAM_GS(4)
+  }
+#undef LOWBIT_STREAM_GS
+#undef LOWBIT_STREAM
 }
 
 template <bool BF16, int FMT>
@@ -495,27 +571,16 @@ static void launch_large_t(GemmArgs& a, hipStream_t st) {
 
 hipError_t launch_gemm(int fmt, bool x_bf16, GemmArgs a, int num_cu, int variant, hipStream_t st) {
   // variant: 0 = automatic, 1 = force large-M kernel, 2 = force small-M kernel (M <= 16)
-  const bool small = small_path(a.M, a.N, a.K, variant);
-  if (small) {
-    SmallPlan p = small_plan(a.M, a.N, a.K, num_cu);
-    a.splits = p.splits;
-    a.gps = p.gps;
+  StreamPlan p;
+  if (variant != 1 && stream_plan(a.M, a.N, a.K, num_cu, &p)) {
     if (fmt == FMT_TERNARY) {
-      if (x_bf16) launch_small_t<true, FMT_TERNARY>(a, p, st);
-      else launch_small_t<false, FMT_TERNARY>(a, p, st);
+      if (x_bf16) launch_stream_t<true, FMT_TERNARY>(a, p, st);
+      else launch_stream_t<false, FMT_TERNARY>(a, p, st);
     } else {
-      if (x_bf16) launch_small_t<true, FMT_BINARY>(a, p, st);
-      else launch_small_t<false, FMT_BINARY>(a, p, st);
-    }
-    if (a.splits > 1) {
-      const int64_t total = (int64_t)a.M * a.N;
-      int grid = (int)((total + 255) / 256);
-      if (grid > 4096) grid = 4096;
-      hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid), dim3(256), 0, st, a);
+      if (x_bf16) launch_stream_t<true, FMT_BINARY>(a, p, st);
+      else launch_stream_t<false, FMT_BINARY>(a, p, st);
     }
   } else {
-    a.splits = 1;
-    a.gps = a.K / 128;
     if (fmt == FMT_TERNARY) {
       if (x_bf16) launch_large_t<true, FMT_TERNARY>(a, st);
       else launch_large_t<false, FMT_TERNARY>(a, st);

@@ -114,7 +114,9 @@ int32_t unpack_lowbit(int32_t format, const uint8_t* packed, int64_t N, int64_t 
                       int8_t* codes, int32_t* invalid_count, void* stream);
 
 /* Workspace bytes lowbit_gemm needs for this problem (0 when none). Depends
- * only on (format, M, N, K) and the current device. */
+ * only on (format, M, N, K) and the current device. Non-zero only for
+ * M <= 16 when K is split across workgroups: a fixed 64 KiB region of
+ * 32-bit counters, one per column tile, followed by the FP32 partial sums. */
 size_t lowbit_gemm_workspace_bytes(int32_t format, int64_t M, int64_t N, int64_t K);
 
 /* The low-bit linear layer (w = scale_g * t from "Representacion y
@@ -138,12 +140,16 @@ size_t lowbit_gemm_workspace_bytes(int32_t format, int64_t M, int64_t N, int64_t
  *               size, ldy >= N; must not overlap X, W, scales, bias
  *   activation  LOWBIT_ACT_NONE or LOWBIT_ACT_GELU_ERF (x * Phi(x), exact erf)
  *   workspace   device scratch of at least lowbit_gemm_workspace_bytes(),
- *               16-byte aligned, any contents; may be NULL when that is 0.
- *               Calls that can run concurrently must not share it.
+ *               256-byte aligned; may be NULL when that is 0. Its bytes must
+ *               be zero before the first call that uses it (allocate it
+ *               zeroed); every call leaves the counters it used at zero
+ *               again, so it can be reused without clearing. Calls that can
+ *               run concurrently (other streams) must not share it.
  *   M, N, K     M, N >= 1; K >= 128 and K % 128 == 0; M, N, K < 2^31
  *
- * Ternary codes 10 are not checked here (hot path); they act as t = 0. The result is deterministic: the same
- * inputs give the same bits on every call on the same device. */
+ * Ternary codes 10 are not checked here (hot path); they act as t = 0.
+ * The result is deterministic: the same inputs give the same bits on every
+ * call on the same device (partial sums are combined in a fixed order). */
 int32_t lowbit_gemm(int32_t format,
                     const void* X, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx,
                     const uint8_t* W_packed, const void* scales, int32_t group, int64_t N,

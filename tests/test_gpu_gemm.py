@@ -168,8 +168,16 @@ def test_special_scales_and_codes(lb):
 
 # ---------------------------------------------------- variants / safety ---
 
+# shapes that reach every compiled variant of the small-M kernel: 4- and
+# 8-wave tiles, slices of 4 .. 32 groups, one or many K splits, odd group
+# counts, ragged N, M < 16
+_SMALL_SHAPES = [(5, 64, 512), (16, 3072, 3072), (7, 520, 6144), (1, 200, 12288),
+                 (16, 8192, 1024), (3, 8200, 2048), (16, 18432, 3072), (2, 8192, 8192),
+                 (16, 100, 16384), (16, 100, 4096), (9, 3000, 2560)]
+
+
 @pytest.mark.parametrize("fmt", ["ternary", "binary"])
-@pytest.mark.parametrize("M,N,K", [(16, 3072, 3072), (7, 512, 9216), (1, 200, 12288)])
+@pytest.mark.parametrize("M,N,K", _SMALL_SHAPES)
 def test_small_and_large_kernels_agree_with_oracle(lb, force_variant, fmt, M, N, K):
     lin = wl.make_linear("both", fmt, M, N, K, seed=500 + M, p0=0.35)
     A, Mg = oracle_linear(lin)
@@ -180,29 +188,38 @@ def test_small_and_large_kernels_agree_with_oracle(lb, force_variant, fmt, M, N,
 
 
 @pytest.mark.parametrize("fmt", ["ternary", "binary"])
-def test_split_k_is_deterministic_and_checks_workspace(lb, fmt):
-    """Split-K calls sum their partials in a fixed order: repeated calls give
-    identical bits, whatever the workspace held before."""
-    M, N, K = 16, 3072, 3072
+@pytest.mark.parametrize("M,N,K", [(16, 3072, 9216), (3, 3072, 12288), (1, 200, 12288)])
+def test_split_k_small_m_is_deterministic_and_reusable(lb, fmt, M, N, K):
+    """Split-K at small M: the workgroups of a column tile combine their FP32
+    partials in split order through the workspace, and the last one resets
+    its counter. Forty calls in a row on one workspace (each into a NaN-filled
+    output) must all write every element and give identical bits; a workspace
+    smaller than required is refused."""
     need = lb.workspace_bytes(fmt, M, N, K)
-    assert need > 0                                   # this shape splits K
-    lin = wl.make_linear("split", fmt, M, N, K, seed=560, p0=0.35)
+    assert need > 0                                   # these shapes split K
+    lin = wl.make_linear("split", fmt, M, N, K, seed=560 + M, p0=0.35)
     x = dev_bits(lin.x, "bf16")
     packed, s = dev_weights(fmt, lin.codes, lin.scales)
-    ws = torch.full((need,), 0xAB, dtype=torch.uint8, device="cuda")
-    outs = [lb.gemm(x, packed, s, fmt, out_dtype=torch.float32, workspace=ws) for _ in range(3)]
+    ws = lb.new_workspace(need)
+    outs = []
+    for _ in range(40):
+        y = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+        lb.gemm(x, packed, s, fmt, out=y, workspace=ws)
+        outs.append(y)
     torch.cuda.synchronize()
+    assert not torch.isnan(outs[0]).any()
     for o in outs[1:]:
         assert torch.equal(o.view(torch.int32), outs[0].view(torch.int32))
+    assert int(ws.count_nonzero()) >= 0                # still a valid tensor
     A, Mg = oracle_linear(lin)
-    _assert_parity(to_host64(outs[0]), A, Mg, "f32", "split-K")
+    _assert_parity(to_host64(outs[0]), A, Mg, "f32", "split-K small M")
     with pytest.raises(ValueError):
         lb.gemm(x, packed, s, fmt, workspace=ws[: need // 2])
 
 
 def test_very_long_k_small_m(lb):
-    """K beyond the small-M kernel's range (258 groups) takes the large-M path."""
-    lin = wl.make_linear("longk", "ternary", 2, 64, 258 * 128, seed=550, p0=0.35)
+    """A long K with an odd group count (129 groups: many splits, a short last one)."""
+    lin = wl.make_linear("longk", "ternary", 2, 64, 129 * 128, seed=550, p0=0.35)
     Y, _ = run_linear(lin)
     A, Mg = oracle_linear(lin)
     _assert_parity(Y, A, Mg, "bf16", "long K")
