@@ -88,6 +88,26 @@ __device__ __forceinline__ void store_out(void* Y, int64_t ldy, int dtype, int m
   else ((float*)Y)[off] = v;
 }
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Direct global -> LDS loads (global_load_lds_*) issued from inline assembly:
+// the address is a wave-uniform 64-bit base (SGPRs) plus a 32-bit per-lane
+// byte offset, and lane l's data lands at LDS byte lds + 16 l (16-byte form)
+// or in the 4-byte slot lds + 4 l, zero-extended (2-byte form). The compiler
+// does not see these as memory operations: the caller waits for them with
+// an explicit s_waitcnt (they count in vmcnt) before reading the LDS.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_ptr_t)p;
+}
+__device__ __forceinline__ void dma_lds16(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(lds), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma_lds2(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_ushort %1, %2" ::"s"(lds), "v"(voff), "s"(sbase)
+               : "memory", "m0");
+}
+
 // ---------------------------------------------------------------------------
 // Code unpacking into MFMA operand registers.
 //

@@ -27,19 +27,27 @@ namespace lowbit {
 // ===========================================================================
 // Large-M kernel (v_mfma_f32_32x32x16): a workgroup computes a 128 x 256 tile
 // of Y with 4 waves side by side along N, each wave 128 x 64 (4 x 2 blocks of
-// 32 x 32). One pipeline stage is one 128-group along K.
+// 32 x 32). One pipeline stage is one 128-group along K; three LDS stages.
 //
-//  * Activations: global -> LDS with direct 16-byte LDS DMA loads
-//    (global_load_lds_dwordx4), three stages in flight. LDS holds each row's
-//    sixteen 16-byte chunks XOR-swizzled by (row % 16), which makes the
-//    fragment reads (32 rows, same chunk) bank-conflict free. Every wave reads
-//    the fragments of a whole group into registers (AGPRs, which MFMA reads
-//    directly); those of group g+1 replace those of group g while the second
-//    column block of group g is computed.
-//  * Packed codes and scales: straight from global memory into VGPRs (each
-//    wave owns distinct columns, so nothing is shared through LDS), one group
-//    ahead of use. A lane loads 16 bytes (ternary) or 8 bytes (binary): the
-//    64 codes its lane group contributes to the group.
+//  * Everything a group needs reaches LDS through direct LDS DMA loads
+//    (global_load_lds, issued from inline assembly with a scalar base and a
+//    loop-invariant lane offset), so no global load writes or reads a
+//    register the loop rewrites, and the only wait on loads in the loop is
+//    the explicit one at each group start (compiler-placed waits on register
+//    loads that cross the loop back-edge drain every load in flight):
+//    - activations: 128 rows x 256 bytes; each row's sixteen 16-byte chunks
+//      are XOR-swizzled by row % 16, which makes the fragment reads (32 rows,
+//      same chunk) bank-conflict free;
+//    - the packed codes of each wave's 64 columns, [column][32 bytes]
+//      (ternary) or [column][16 bytes] (binary);
+//    - each wave's 64 fp16 scales, one 4-byte LDS slot each.
+//  * At the start of group g a wave waits until only its loads of stage g+1
+//    are in flight (stage g was issued two groups earlier), passes the
+//    barrier, and issues stage g+2 into the buffer of group g-1.
+//  * Per MFMA step the wave reads the four A fragments of the next step while
+//    the eight MFMAs of the current step run; the B operands of the step are
+//    unpacked from the group's codes (one 16- or 8-byte LDS read per column
+//    block and group).
 //  * Group scales, Horner form: the MFMAs accumulate in units of the current
 //    group's scale c_g = +-s_g / 2, and at each group boundary the accumulator
 //    is rescaled by c_{g-1} / c_g (one FP32 multiply per element); after the
@@ -57,16 +65,22 @@ namespace lowbit {
 namespace large {
 constexpr int BM = 128, BN = 256, THREADS = 256, STAGES = 3;
 constexpr int ROW_BYTES = 256;                 // 128 k x 2 bytes
-constexpr int STAGE_BYTES = BM * ROW_BYTES;    // 32 KiB
+constexpr int X_BYTES = BM * ROW_BYTES;        // activations per stage (32 KiB)
+constexpr int W_BYTES = BN * 32;               // packed codes per stage (8 KiB ternary)
+constexpr int S_BYTES = BN * 4;                // scales per stage
+constexpr int STAGE_BYTES = X_BYTES + W_BYTES + S_BYTES;
+// DMA loads per wave and stage: 8 (activations) + 2 or 1 (codes) + 1 (scales)
+template <bool TERN>
+constexpr int stage_loads() { return TERN ? 11 : 10; }
+// s_waitcnt immediate for vmcnt(n), expcnt(7), lgkmcnt(0)
+constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | ((n >> 4) << 14); }
 }  // namespace large
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 template <bool BF16, int FMT>
 __global__ __launch_bounds__(256, 1) void gemm_large_kernel(GemmArgs a, int tiles_m, int tiles_n) {
   using namespace large;
   constexpr bool TERN = FMT == FMT_TERNARY;
-  __shared__ __align__(16) uint8_t sA[STAGES][STAGE_BYTES];
+  __shared__ __align__(16) uint8_t smem[STAGES][STAGE_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, q = lane >> 5, r32 = lane & 31;
@@ -81,43 +95,47 @@ __global__ __launch_bounds__(256, 1) void gemm_large_kernel(GemmArgs a, int tile
   const int G = a.K >> 7;
   const int64_t wrow = TERN ? (a.K >> 2) : (a.K >> 3);
   const float factor = code_factor<TERN>();
+  const int wcol0 = n0 + 64 * wave;                     // first column of this wave
 
-  // ---- activation stage g -> LDS buffer `buf` (wave w: rows 32w .. 32w+31) ----
-  auto dma = [&](int g, int buf) {
+  // ---- stage g -> LDS buffer `buf` (DMA only) ----
+  // Per-lane byte offsets are computed once; per group only the wave-uniform
+  // base pointers move (the loads then address as scalar base + 32-bit lane
+  // offset, and no vector register a DMA in flight reads is rewritten).
+  uint32_t xoff[8];
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int rb = 32 * wave + 4 * it;                    // wave-uniform first row
-      const int r = rb + (lane >> 4);
-      const int c = (lane & 15) ^ (r & 15);                 // chunk stored in slot lane&15
-      const int m = min(m0 + r, a.M - 1);                   // rows past M: any valid row
-      const uint16_t* src = a.X + (int64_t)m * a.ldx + (g << 7) + 8 * c;
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr_t)(sA[buf] + rb * ROW_BYTES), 16, 0, 0);
-    }
+  for (int it = 0; it < 8; ++it) {
+    const int r = 32 * wave + 4 * it + (lane >> 4);
+    const int c = (lane & 15) ^ (r & 15);               // chunk stored in slot lane&15
+    const int m = min(m0 + r, a.M - 1);                 // rows past M: any valid row
+    xoff[it] = (uint32_t)(((int64_t)m * a.ldx + 8 * c) * 2);
+  }
+  uint32_t woff[2], soff;
+  if (TERN) {
+#pragma unroll
+    for (int it = 0; it < 2; ++it)                      // columns past N: any valid column
+      woff[it] = (uint32_t)(min(wcol0 + 32 * it + (lane >> 1), a.N - 1) * wrow + 16 * (lane & 1));
+  } else {
+    woff[0] = woff[1] = (uint32_t)(min(wcol0 + lane, a.N - 1) * wrow);
+  }
+  soff = (uint32_t)(min(wcol0 + lane, a.N - 1) * (int64_t)G * 2);
+  auto stage = [&](int g, int buf) {
+    uint8_t* base = smem[buf];
+    const uint8_t* xg = (const uint8_t*)a.X + ((int64_t)g << 8);
+#pragma unroll
+    for (int it = 0; it < 8; ++it)
+      dma_lds16(xg, xoff[it], lds_addr(base + (32 * wave + 4 * it) * ROW_BYTES));
+    uint8_t* wb = base + X_BYTES + wave * (64 * 32);
+    const uint8_t* wg = a.W + g * (TERN ? 32 : 16);
+    dma_lds16(wg, woff[0], lds_addr(wb));
+    if (TERN) dma_lds16(wg, woff[1], lds_addr(wb + 1024));
+    // scales: lane l -> 4-byte slot l (2-byte load, zero-extended)
+    dma_lds2((const uint8_t*)a.S + 2 * g, soff, lds_addr(base + X_BYTES + W_BYTES + wave * 256));
   };
-  auto afrag = [&](int buf, int i, int s) -> u32x4 {
+
+  auto afrag = [&](const uint8_t* xb, int i, int s) -> u32x4 {
     const int r = 32 * i + r32;
     const int p = (8 * q + s) ^ (r & 15);
-    return *(const u32x4*)(sA[buf] + r * ROW_BYTES + p * 16);
-  };
-
-  // ---- packed codes + scales of this lane's two columns ----
-  int ncol[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) ncol[j] = min(n0 + 64 * wave + 32 * j + r32, a.N - 1);
-  // raw scale bits are kept until the group starts: converting them at load
-  // time would make the wave wait for the load (and everything issued before)
-  auto bload = [&](int g, u32x4 (&bw)[2], uint16_t (&sb)[2]) {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint8_t* p = a.W + (int64_t)ncol[j] * wrow;
-      if (TERN) {
-        bw[j] = *(const u32x4*)(p + g * 32 + 16 * q);
-      } else {
-        u32x2 v = *(const u32x2*)(p + g * 16 + 8 * q);
-        bw[j] = u32x4{v[0], v[1], 0u, 0u};
-      }
-      sb[j] = a.S[(int64_t)ncol[j] * G + g];
-    }
+    return *(const u32x4*)(xb + r * ROW_BYTES + p * 16);
   };
 
   f32x16 acc[4][2];
@@ -127,72 +145,64 @@ __global__ __launch_bounds__(256, 1) void gemm_large_kernel(GemmArgs a, int tile
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
   float cref[2] = {1.0f, 1.0f};                 // reference scale of the accumulator
 
-  u32x4 A[4][8];
+  stage(0, 0);
+  stage(min(1, G - 1), 1);
+  int buf = 0;
+  for (int g = 0; g < G; ++g) {
+    // stage g complete (only this wave's stage g+1 loads may be in flight),
+    // and every wave's part of it visible
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(stage_loads<TERN>()));
+    __syncthreads();
+    // past the end this copies the last group into a buffer nobody reads
+    stage(min(g + 2, G - 1), buf == 0 ? 2 : buf - 1);
+    const uint8_t* xb = smem[buf];
+    const uint8_t* wb = smem[buf] + X_BYTES + wave * (64 * 32);
+    const uint8_t* sbuf = smem[buf] + X_BYTES + W_BYTES + wave * 256;
 
-  // one column block of one group: rescale to the group's scale, then 32 MFMAs
-  auto block = [&](int j, const u32x4 (&bw)[2], const uint16_t (&sb)[2], bool refill, int nbuf) {
-    const float s = factor * half_bits_to_float(sb[j]);
-    const bool zero = s == 0.0f;
-    const float r = zero ? 1.0f : cref[j] / s;
-    cref[j] = zero ? cref[j] : s;
-    const uint32_t tm = zero ? 0u : TERN_MASK;
-    const uint32_t mk = zero ? 0u : BIN_SIGN, bs = zero ? 0u : BIN_TWO;
+    // codes, scale and Horner rescale of each column block
+    u32x4 bw[2];
+    uint32_t tm[2], mk[2], bs[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i][j] *= r;
+    for (int j = 0; j < 2; ++j) {
+      const int col = 32 * j + r32;
+      if (TERN) {
+        bw[j] = *(const u32x4*)(wb + col * 32 + 16 * q);
+      } else {
+        const u32x2 v = *(const u32x2*)(wb + col * 16 + 8 * q);
+        bw[j] = u32x4{v[0], v[1], 0u, 0u};
+      }
+      const float sc = factor * half_bits_to_float((uint16_t)*(const uint32_t*)(sbuf + col * 4));
+      const bool zero = sc == 0.0f;
+      const float r = zero ? 1.0f : cref[j] / sc;
+      cref[j] = zero ? cref[j] : sc;
+      tm[j] = zero ? 0u : TERN_MASK;
+      mk[j] = zero ? 0u : BIN_SIGN;
+      bs[j] = zero ? 0u : BIN_TWO;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i][j] *= r;
+    }
+
+    // eight MFMA steps; the A fragments of step st+1 are read during step st
+    u32x4 A[2][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) A[0][i] = afrag(xb, i, 0);
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
-      const u32x4 bf = TERN ? tern_chunk(bw[j][st >> 1], st & 1, tm)
-                            : bin_chunk(bw[j][st >> 2], st & 3, mk, bs);
+      if (st < 7) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i][j] = mfma32<BF16>(A[i][st], bf, acc[i][j]);
-      if (refill) {
+        for (int i = 0; i < 4; ++i) A[(st + 1) & 1][i] = afrag(xb, i, st + 1);
+      }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) A[i][st] = afrag(nbuf, i, st);
+      for (int j = 0; j < 2; ++j) {
+        const u32x4 bf = TERN ? tern_chunk(bw[j][st >> 1], st & 1, tm[j])
+                              : bin_chunk(bw[j][st >> 2], st & 3, mk[j], bs[j]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i][j] = mfma32<BF16>(A[st & 1][i], bf, acc[i][j]);
       }
     }
-  };
-
-  // One group. At its start a single wait + barrier covers everything issued
-  // at the start of the previous group (codes and scales of this group, the
-  // activation stage of the next one); then the codes and scales of group
-  // g+1 (into the other register set: the loop is unrolled by two) and the
-  // activation stage of group g+2 are issued, so every global load has a whole
-  // group of compute to arrive. Column block 1 replaces the fragments of
-  // group g by those of group g+1 as it goes.
-  auto group = [&](int g, const u32x4 (&bw)[2], const uint16_t (&sb)[2], u32x4 (&bwn)[2],
-                   uint16_t (&sbn)[2]) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    const bool more = g + 1 < G;
-    if (more) {
-      bload(g + 1, bwn, sbn);
-      // past the end this reloads the last group into the buffer of group
-      // g-1, which nobody reads any more
-      dma(min(g + 2, G - 1), (g + 2) % STAGES);
-    }
-    block(0, bw, sb, false, 0);
-    if (more) block(1, bw, sb, true, (g + 1) % STAGES);
-    else block(1, bw, sb, false, 0);
-  };
-
-  u32x4 bw0[2], bw1[2];
-  uint16_t sb0[2], sb1[2];
-
-  // prologue: stages 0 and 1 in flight, group-0 codes, then group-0 fragments
-  dma(0, 0);
-  if (G > 1) dma(1, 1);
-  bload(0, bw0, sb0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int st = 0; st < 8; ++st) A[i][st] = afrag(0, i, st);
-
-  for (int g = 0; g < G; g += 2) {
-    group(g, bw0, sb0, bw1, sb1);
-    if (g + 1 < G) group(g + 1, bw1, sb1, bw0, sb0);
+    buf = buf == 2 ? 0 : buf + 1;
   }
+  __builtin_amdgcn_s_waitcnt(0);                       // no DMA may still write LDS
 
   // ---- epilogue: final scale, bias, activation, one RNE cast, store ----
   const bool y16 = a.y_dtype != DT_F32;
@@ -202,7 +212,7 @@ __global__ __launch_bounds__(256, 1) void gemm_large_kernel(GemmArgs a, int tile
     // 16-byte chunks XOR-swizzled by row % 8) and leave as 16-byte stores
     // covering whole 128-byte row segments.
     __syncthreads();                                  // LDS stages are free now
-    uint8_t* sY = sA[0] + wave * (128 * 128);
+    uint8_t* sY = &smem[0][0] + wave * (128 * 128);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int n = n0 + 64 * wave + 32 * j + r32;
