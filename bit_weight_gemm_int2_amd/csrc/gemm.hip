@@ -25,9 +25,10 @@
 namespace lowbit {
 
 // ===========================================================================
-// Large-M kernel (v_mfma_f32_32x32x16): a workgroup computes a 128 x 256 tile
-// of Y with 4 waves side by side along N, each wave 128 x 64 (4 x 2 blocks of
-// 32 x 32). One pipeline stage is one 128-group along K; three LDS stages.
+// Large-M kernel (v_mfma_f32_32x32x16): a workgroup computes a 128 x 64 WN
+// tile of Y with WN waves side by side along N (WN = 8: two waves per SIMD;
+// WN = 4 for narrow N), each wave 128 x 64 (4 x 2 blocks of 32 x 32). One
+// pipeline stage is one 128-group along K; three LDS stages.
 //
 //  * Everything a group needs reaches LDS through direct LDS DMA loads
 //    (global_load_lds, issued from inline assembly with a scalar base and a
@@ -63,23 +64,28 @@ namespace lowbit {
 // MFMA step s (0..7) uses its slots 64q + 8s .. +7.
 // ===========================================================================
 namespace large {
-constexpr int BM = 128, BN = 256, THREADS = 256, STAGES = 3;
+// WN waves side by side along N: a tile is BM x 64 WN
+constexpr int BM = 128, STAGES = 3;
 constexpr int ROW_BYTES = 256;                 // 128 k x 2 bytes
 constexpr int X_BYTES = BM * ROW_BYTES;        // activations per stage (32 KiB)
-constexpr int W_BYTES = BN * 32;               // packed codes per stage (8 KiB ternary)
-constexpr int S_BYTES = BN * 4;                // scales per stage
-constexpr int STAGE_BYTES = X_BYTES + W_BYTES + S_BYTES;
-// DMA loads per wave and stage: 8 (activations) + 2 or 1 (codes) + 1 (scales)
-template <bool TERN>
-constexpr int stage_loads() { return TERN ? 11 : 10; }
+template <int WN> constexpr int bn() { return 64 * WN; }
+template <int WN> constexpr int w_bytes() { return bn<WN>() * 32; }   // packed codes (ternary size)
+template <int WN> constexpr int s_bytes() { return bn<WN>() * 4; }    // scales, 4-byte slots
+template <int WN> constexpr int stage_bytes() { return X_BYTES + w_bytes<WN>() + s_bytes<WN>(); }
+// DMA loads per wave and stage: activations (128 rows, 4 per load, split
+// over the waves) + codes (2 ternary, 1 binary) + scales (1)
+template <bool TERN, int WN>
+constexpr int stage_loads() { return 32 / WN + (TERN ? 2 : 1) + 1; }
 // s_waitcnt immediate for vmcnt(n), expcnt(7), lgkmcnt(0)
 constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | ((n >> 4) << 14); }
 }  // namespace large
 
-template <bool BF16, int FMT>
-__global__ __launch_bounds__(256, 1) void gemm_large_kernel(GemmArgs a, int tiles_m, int tiles_n) {
+template <bool BF16, int FMT, int WN>
+__global__ __launch_bounds__(64 * WN) void gemm_large_kernel(GemmArgs a, int tiles_m, int tiles_n) {
   using namespace large;
   constexpr bool TERN = FMT == FMT_TERNARY;
+  constexpr int BN = bn<WN>(), XR = 32 / WN;            // activation loads per wave and stage
+  constexpr int W_BYTES = w_bytes<WN>(), STAGE_BYTES = stage_bytes<WN>();
   __shared__ __align__(16) uint8_t smem[STAGES][STAGE_BYTES];
 
   const int tid = threadIdx.x;
@@ -101,10 +107,10 @@ __global__ __launch_bounds__(256, 1) void gemm_large_kernel(GemmArgs a, int tile
   // Per-lane byte offsets are computed once; per group only the wave-uniform
   // base pointers move (the loads then address as scalar base + 32-bit lane
   // offset, and no vector register a DMA in flight reads is rewritten).
-  uint32_t xoff[8];
+  uint32_t xoff[XR];
 #pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    const int r = 32 * wave + 4 * it + (lane >> 4);
+  for (int it = 0; it < XR; ++it) {
+    const int r = 4 * XR * wave + 4 * it + (lane >> 4);
     const int c = (lane & 15) ^ (r & 15);               // chunk stored in slot lane&15
     const int m = min(m0 + r, a.M - 1);                 // rows past M: any valid row
     xoff[it] = (uint32_t)(((int64_t)m * a.ldx + 8 * c) * 2);
@@ -122,8 +128,8 @@ __global__ __launch_bounds__(256, 1) void gemm_large_kernel(GemmArgs a, int tile
     uint8_t* base = smem[buf];
     const uint8_t* xg = (const uint8_t*)a.X + ((int64_t)g << 8);
 #pragma unroll
-    for (int it = 0; it < 8; ++it)
-      dma_lds16(xg, xoff[it], lds_addr(base + (32 * wave + 4 * it) * ROW_BYTES));
+    for (int it = 0; it < XR; ++it)
+      dma_lds16(xg, xoff[it], lds_addr(base + (4 * XR * wave + 4 * it) * ROW_BYTES));
     uint8_t* wb = base + X_BYTES + wave * (64 * 32);
     const uint8_t* wg = a.W + g * (TERN ? 32 : 16);
     dma_lds16(wg, woff[0], lds_addr(wb));
@@ -151,7 +157,7 @@ __global__ __launch_bounds__(256, 1) void gemm_large_kernel(GemmArgs a, int tile
   for (int g = 0; g < G; ++g) {
     // stage g complete (only this wave's stage g+1 loads may be in flight),
     // and every wave's part of it visible
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(stage_loads<TERN>()));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(stage_loads<TERN, WN>()));
     __syncthreads();
     // past the end this copies the last group into a buffer nobody reads
     stage(min(g + 2, G - 1), buf == 0 ? 2 : buf - 1);
@@ -573,10 +579,18 @@ static void launch_stream_t(const GemmArgs& a, const StreamPlan& p, hipStream_t 
 #undef LOWBIT_STREAM
 }
 
+// Large-M tiles: 128 x 512 (8 waves, two per SIMD) when N is wide enough,
+// else 128 x 256 (4 waves).
 template <bool BF16, int FMT>
 static void launch_large_t(GemmArgs& a, hipStream_t st) {
-  const int tm = (a.M + large::BM - 1) / large::BM, tn = (a.N + large::BN - 1) / large::BN;
-  hipLaunchKernelGGL((gemm_large_kernel<BF16, FMT>), dim3(tm * tn), dim3(large::THREADS), 0, st, a, tm, tn);
+  const int tm = (a.M + large::BM - 1) / large::BM;
+  if (a.N >= 2048) {
+    const int tn = (a.N + large::bn<8>() - 1) / large::bn<8>();
+    hipLaunchKernelGGL((gemm_large_kernel<BF16, FMT, 8>), dim3(tm * tn), dim3(512), 0, st, a, tm, tn);
+  } else {
+    const int tn = (a.N + large::bn<4>() - 1) / large::bn<4>();
+    hipLaunchKernelGGL((gemm_large_kernel<BF16, FMT, 4>), dim3(tm * tn), dim3(256), 0, st, a, tm, tn);
+  }
 }
 
 hipError_t launch_gemm(int fmt, bool x_bf16, GemmArgs a, int num_cu, int variant, hipStream_t st) {
