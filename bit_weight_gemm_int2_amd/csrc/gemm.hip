@@ -40,7 +40,9 @@ namespace lowbit {
 //      are XOR-swizzled by row % 16, which makes the fragment reads (32 rows,
 //      same chunk) bank-conflict free;
 //    - the packed codes of each wave's 64 columns, [column][32 bytes]
-//      (ternary) or [column][16 bytes] (binary);
+//      (ternary; the two 16-byte halves swapped when bit 3 of the column is
+//      set, which keeps the fragment reads bank-conflict free) or
+//      [column][16 bytes] (binary);
 //    - each wave's 64 fp16 scales, one 4-byte LDS slot each.
 //  * At the start of group g a wave waits until only its loads of stage g+1
 //    are in flight (stage g was issued two groups earlier), passes the
@@ -117,9 +119,13 @@ __global__ __launch_bounds__(64 * WN) void gemm_large_kernel(GemmArgs a, int til
   }
   uint32_t woff[2], soff;
   if (TERN) {
+    // LDS slot h of local column c holds 16-byte half h ^ bit 3 of c, so the
+    // fragment reads (16 consecutive columns, same half) hit distinct banks
 #pragma unroll
-    for (int it = 0; it < 2; ++it)                      // columns past N: any valid column
-      woff[it] = (uint32_t)(min(wcol0 + 32 * it + (lane >> 1), a.N - 1) * wrow + 16 * (lane & 1));
+    for (int it = 0; it < 2; ++it) {                    // columns past N: any valid column
+      const int c = 32 * it + (lane >> 1);
+      woff[it] = (uint32_t)(min(wcol0 + c, a.N - 1) * wrow + 16 * ((lane & 1) ^ ((c >> 3) & 1)));
+    }
   } else {
     woff[0] = woff[1] = (uint32_t)(min(wcol0 + lane, a.N - 1) * wrow);
   }
@@ -172,7 +178,7 @@ __global__ __launch_bounds__(64 * WN) void gemm_large_kernel(GemmArgs a, int til
     for (int j = 0; j < 2; ++j) {
       const int col = 32 * j + r32;
       if (TERN) {
-        bw[j] = *(const u32x4*)(wb + col * 32 + 16 * q);
+        bw[j] = *(const u32x4*)(wb + col * 32 + 16 * (q ^ ((col >> 3) & 1)));
       } else {
         const u32x2 v = *(const u32x2*)(wb + col * 16 + 8 * q);
         bw[j] = u32x4{v[0], v[1], 0u, 0u};
