@@ -12,7 +12,7 @@ the launch stream), the CPU oracle timed on a bounded sample (cpu_baseline),
 and the small-M weight-streaming GB/s over a 100-linear MMDiT weight set at
 M = 16 and M = 1 (small_m).
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu] [--no-small]
+    python bench.py [--gpus 1] [--steps 100] [--warmup 300] [--no-cpu] [--no-small]
 """
 from __future__ import annotations
 
@@ -75,14 +75,15 @@ def bench_large(torch, lb, steps, warmup):
     sd = dev16(torch, down.scales, torch.float16)
     h = torch.empty((M, N1), dtype=torch.bfloat16, device="cuda")
     y = torch.empty((M, N2), dtype=torch.bfloat16, device="cuda")
+    ws = lb.new_workspace(max(lb.workspace_bytes("ternary", M, N1, K1), lb.workspace_bytes("ternary", M, N2, N1)))
 
     def step(evs=None):
         if evs is not None:
             evs[0].record()
-        lb.gemm(x, pu, su, "ternary", activation="gelu", out=h)
+        lb.gemm(x, pu, su, "ternary", activation="gelu", out=h, workspace=ws)
         if evs is not None:
             evs[1].record()
-        lb.gemm(h, pd, sd, "ternary", out=y)
+        lb.gemm(h, pd, sd, "ternary", out=y, workspace=ws)
         if evs is not None:
             evs[2].record()
 
@@ -153,7 +154,8 @@ def bench_small(torch, lb, reps=10):
             graph = torch.cuda.CUDAGraph()
             with torch.cuda.graph(graph):
                 sweep()
-            graph.replay()
+            for _ in range(20):                       # warm replays (clocks settle)
+                graph.replay()
             torch.cuda.synchronize()
             t0 = torch.cuda.Event(enable_timing=True)
             t1 = torch.cuda.Event(enable_timing=True)
@@ -228,8 +230,8 @@ def cpu_baseline(seconds_target=10.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-small", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true",

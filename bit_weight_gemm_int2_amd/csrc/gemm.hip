@@ -53,10 +53,11 @@ namespace lowbit {
 //    block and group).
 //  * Group scales, Horner form: the MFMAs accumulate in units of the current
 //    group's scale c_g = +-s_g / 2, and at each group boundary the accumulator
-//    is rescaled by c_{g-1} / c_g (one FP32 multiply per element); after the
-//    last group it is multiplied by c_G. In exact arithmetic this is
-//    sum_g c_g P_g; in FP32 each rescale adds one rounding (about 2G ulps of
-//    relative error over the whole sum, far inside the 1e-3 tolerance). A
+//    is rescaled by c_{g-1} / c_g (one FP32 multiply per element; the ratio
+//    itself from the hardware reciprocal); after the last group it is
+//    multiplied by c_G. In exact arithmetic this is sum_g c_g P_g; in FP32
+//    each rescale adds a few roundings (about 4G ulps of relative error over
+//    the whole sum, far inside the 1e-3 tolerance). A
 //    group whose scale is zero is fed as zero codes and keeps the previous
 //    reference scale, so zero and subnormal scales are exact. Requires finite
 //    scales and |partial sums| < 2^100 (the quotient of two FP16 scales is at
@@ -185,7 +186,10 @@ __global__ __launch_bounds__(64 * WN) void gemm_large_kernel(GemmArgs a, int til
       }
       const float sc = factor * half_bits_to_float((uint16_t)*(const uint32_t*)(sbuf + col * 4));
       const bool zero = sc == 0.0f;
-      const float r = zero ? 1.0f : cref[j] / sc;
+      // ratio of the old to the new reference scale, by the hardware
+      // reciprocal (1 ulp): deterministic, and its error is one more
+      // rounding-size term per group, far inside the accuracy bound
+      const float r = zero ? 1.0f : cref[j] * __builtin_amdgcn_rcpf(sc);
       cref[j] = zero ? cref[j] : sc;
       tm[j] = zero ? 0u : TERN_MASK;
       mk[j] = zero ? 0u : BIN_SIGN;
