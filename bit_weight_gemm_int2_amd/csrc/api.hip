@@ -63,6 +63,8 @@ int force_variant() {
   if (!v) return 0;
   if (!std::strcmp(v, "large")) return 1;
   if (!std::strcmp(v, "small")) return 2;
+  if (!std::strcmp(v, "large-wide")) return 5;
+  if (!std::strcmp(v, "large-pair")) return 6;
   return 0;
 }
 

@@ -25,10 +25,13 @@
 namespace lowbit {
 
 // ===========================================================================
-// Large-M kernel (v_mfma_f32_32x32x16): a workgroup computes a 128 x 64 WN
-// tile of Y with WN waves side by side along N (WN = 8: two waves per SIMD;
-// WN = 4 for narrow N), each wave 128 x 64 (4 x 2 blocks of 32 x 32). One
-// pipeline stage is one 128-group along K; three LDS stages.
+// Large-M kernel (v_mfma_f32_32x32x16): a workgroup computes a BMT x 64 WN
+// tile of Y with WN waves side by side along N, each wave BMT x 64 (BMT/32
+// x 2 blocks of 32 x 32). One pipeline stage is one 128-group along K.
+// Configurations (chosen per shape by the launcher):
+//  * BMT = 128, WN = 8 (two waves per SIMD), three LDS stages: one
+//    workgroup per CU (WN = 4 for narrow N);
+//  * BMT = 96, WN = 4, two stages: two workgroups per CU.
 //
 //  * Everything a group needs reaches LDS through direct LDS DMA loads
 //    (global_load_lds, issued from inline assembly with a scalar base and a
@@ -36,7 +39,7 @@ namespace lowbit {
 //    register the loop rewrites, and the only wait on loads in the loop is
 //    the explicit one at each group start (compiler-placed waits on register
 //    loads that cross the loop back-edge drain every load in flight):
-//    - activations: 128 rows x 256 bytes; each row's sixteen 16-byte chunks
+//    - activations: BMT rows x 256 bytes; each row's sixteen 16-byte chunks
 //      are XOR-swizzled by row % 16, which makes the fragment reads (32 rows,
 //      same chunk) bank-conflict free;
 //    - the packed codes of each wave's 64 columns, [column][32 bytes]
@@ -44,11 +47,14 @@ namespace lowbit {
 //      set, which keeps the fragment reads bank-conflict free) or
 //      [column][16 bytes] (binary);
 //    - each wave's 64 fp16 scales, one 4-byte LDS slot each.
-//  * At the start of group g a wave waits until only its loads of stage g+1
-//    are in flight (stage g was issued two groups earlier), passes the
-//    barrier, and issues stage g+2 into the buffer of group g-1.
-//  * Per MFMA step the wave reads the four A fragments of the next step while
-//    the eight MFMAs of the current step run; the B operands of the step are
+//  * Three stages: at the start of group g a wave waits until only its
+//    loads of stage g+1 are in flight (stage g was issued two groups
+//    earlier), passes the barrier, and issues stage g+2 into the buffer of
+//    group g-1. Two stages: it waits for all its loads (stage g, issued one
+//    group earlier), passes the barrier and issues stage g+1 into the buffer
+//    of group g-1.
+//  * Per MFMA step the wave reads the A fragments of the next step while
+//    the MFMAs of the current step run; the B operands of the step are
 //    unpacked from the group's codes (one 16- or 8-byte LDS read per column
 //    block and group).
 //  * Group scales, Horner form: the MFMAs accumulate in units of the current
@@ -67,29 +73,33 @@ namespace lowbit {
 // MFMA step s (0..7) uses its slots 64q + 8s .. +7.
 // ===========================================================================
 namespace large {
-// WN waves side by side along N: a tile is BM x 64 WN
+// WN waves side by side along N: a tile is BMT x 64 WN (BMT = 128 by default)
 constexpr int BM = 128, STAGES = 3;
 constexpr int ROW_BYTES = 256;                 // 128 k x 2 bytes
-constexpr int X_BYTES = BM * ROW_BYTES;        // activations per stage (32 KiB)
+template <int BMT> constexpr int x_bytes() { return BMT * ROW_BYTES; }   // activations per stage
 template <int WN> constexpr int bn() { return 64 * WN; }
 template <int WN> constexpr int w_bytes() { return bn<WN>() * 32; }   // packed codes (ternary size)
 template <int WN> constexpr int s_bytes() { return bn<WN>() * 4; }    // scales, 4-byte slots
-template <int WN> constexpr int stage_bytes() { return X_BYTES + w_bytes<WN>() + s_bytes<WN>(); }
-// DMA loads per wave and stage: activations (128 rows, 4 per load, split
+template <int WN, int BMT> constexpr int stage_bytes() { return x_bytes<BMT>() + w_bytes<WN>() + s_bytes<WN>(); }
+// DMA loads per wave and stage: activations (BMT rows, 4 per load, split
 // over the waves) + codes (2 ternary, 1 binary) + scales (1)
-template <bool TERN, int WN>
-constexpr int stage_loads() { return 32 / WN + (TERN ? 2 : 1) + 1; }
+template <bool TERN, int WN, int BMT>
+constexpr int stage_loads() { return BMT / (4 * WN) + (TERN ? 2 : 1) + 1; }
 // s_waitcnt immediate for vmcnt(n), expcnt(7), lgkmcnt(0)
 constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | ((n >> 4) << 14); }
 }  // namespace large
 
-template <bool BF16, int FMT, int WN>
+template <bool BF16, int FMT, int WN, int BMT = 128, int NST = 3>
 __global__ __launch_bounds__(64 * WN) void gemm_large_kernel(GemmArgs a, int tiles_m, int tiles_n) {
   using namespace large;
   constexpr bool TERN = FMT == FMT_TERNARY;
-  constexpr int BN = bn<WN>(), XR = 32 / WN;            // activation loads per wave and stage
-  constexpr int W_BYTES = w_bytes<WN>(), STAGE_BYTES = stage_bytes<WN>();
-  __shared__ __align__(16) uint8_t smem[STAGES][STAGE_BYTES];
+  constexpr int BN = bn<WN>(), XR = BMT / (4 * WN);     // activation loads per wave and stage
+  constexpr int IB = BMT / 32;                          // 32-row blocks per wave
+  constexpr int X_BYTES = x_bytes<BMT>(), W_BYTES = w_bytes<WN>(), STAGE_BYTES = stage_bytes<WN, BMT>();
+  static_assert(NST == 2 || NST == 3, "two or three stages");
+  static_assert(BMT % (4 * WN) == 0 && BMT % 32 == 0, "tile height");
+  static_assert(WN * BMT * 128 <= NST * STAGE_BYTES, "epilogue staging fits in the stages");
+  __shared__ __align__(16) uint8_t smem[NST][STAGE_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, q = lane >> 5, r32 = lane & 31;
@@ -100,7 +110,7 @@ __global__ __launch_bounds__(64 * WN) void gemm_large_kernel(GemmArgs a, int til
   int t = blockIdx.x;
   const int T = tiles_m * tiles_n;
   if ((T & 7) == 0) t = (t & 7) * (T >> 3) + (t >> 3);
-  const int m0 = (t / tiles_n) * BM, n0 = (t % tiles_n) * BN;
+  const int m0 = (t / tiles_n) * BMT, n0 = (t % tiles_n) * BN;
   const int G = a.K >> 7;
   const int64_t wrow = TERN ? (a.K >> 2) : (a.K >> 3);
   const float factor = code_factor<TERN>();
@@ -151,23 +161,24 @@ __global__ __launch_bounds__(64 * WN) void gemm_large_kernel(GemmArgs a, int til
     return *(const u32x4*)(xb + r * ROW_BYTES + p * 16);
   };
 
-  f32x16 acc[4][2];
+  f32x16 acc[IB][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < IB; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
   float cref[2] = {1.0f, 1.0f};                 // reference scale of the accumulator
 
   stage(0, 0);
-  stage(min(1, G - 1), 1);
+  if (NST == 3) stage(min(1, G - 1), 1);
   int buf = 0;
   for (int g = 0; g < G; ++g) {
-    // stage g complete (only this wave's stage g+1 loads may be in flight),
-    // and every wave's part of it visible
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(stage_loads<TERN, WN>()));
+    // stage g complete (three stages: only this wave's stage g+1 loads may
+    // be in flight), and every wave's part of it visible
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(NST == 3 ? stage_loads<TERN, WN, BMT>() : 0));
     __syncthreads();
     // past the end this copies the last group into a buffer nobody reads
-    stage(min(g + 2, G - 1), buf == 0 ? 2 : buf - 1);
+    if (NST == 3) stage(min(g + 2, G - 1), buf == 0 ? 2 : buf - 1);
+    else stage(min(g + 1, G - 1), buf ^ 1);
     const uint8_t* xb = smem[buf];
     const uint8_t* wb = smem[buf] + X_BYTES + wave * (64 * 32);
     const uint8_t* sbuf = smem[buf] + X_BYTES + W_BYTES + wave * 256;
@@ -195,28 +206,28 @@ __global__ __launch_bounds__(64 * WN) void gemm_large_kernel(GemmArgs a, int til
       mk[j] = zero ? 0u : BIN_SIGN;
       bs[j] = zero ? 0u : BIN_TWO;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i][j] *= r;
+      for (int i = 0; i < IB; ++i) acc[i][j] *= r;
     }
 
     // eight MFMA steps; the A fragments of step st+1 are read during step st
-    u32x4 A[2][4];
+    u32x4 A[2][IB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) A[0][i] = afrag(xb, i, 0);
+    for (int i = 0; i < IB; ++i) A[0][i] = afrag(xb, i, 0);
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
       if (st < 7) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) A[(st + 1) & 1][i] = afrag(xb, i, st + 1);
+        for (int i = 0; i < IB; ++i) A[(st + 1) & 1][i] = afrag(xb, i, st + 1);
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const u32x4 bf = TERN ? tern_chunk(bw[j][st >> 1], st & 1, tm[j])
                               : bin_chunk(bw[j][st >> 2], st & 3, mk[j], bs[j]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i][j] = mfma32<BF16>(A[st & 1][i], bf, acc[i][j]);
+        for (int i = 0; i < IB; ++i) acc[i][j] = mfma32<BF16>(A[st & 1][i], bf, acc[i][j]);
       }
     }
-    buf = buf == 2 ? 0 : buf + 1;
+    buf = NST == 3 ? (buf == 2 ? 0 : buf + 1) : buf ^ 1;
   }
   __builtin_amdgcn_s_waitcnt(0);                       // no DMA may still write LDS
 
@@ -228,7 +239,7 @@ __global__ __launch_bounds__(64 * WN) void gemm_large_kernel(GemmArgs a, int til
     // 16-byte chunks XOR-swizzled by row % 8) and leave as 16-byte stores
     // covering whole 128-byte row segments.
     __syncthreads();                                  // LDS stages are free now
-    uint8_t* sY = &smem[0][0] + wave * (128 * 128);
+    uint8_t* sY = &smem[0][0] + wave * (BMT * 128);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int n = n0 + 64 * wave + 32 * j + r32;
@@ -236,7 +247,7 @@ __global__ __launch_bounds__(64 * WN) void gemm_large_kernel(GemmArgs a, int til
       const float c = cref[j];
       const int col = 32 * j + r32;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < IB; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = 32 * i + 8 * (r >> 2) + 4 * q + (r & 3);
@@ -248,7 +259,7 @@ __global__ __launch_bounds__(64 * WN) void gemm_large_kernel(GemmArgs a, int til
     }
     __syncthreads();                                  // staged tile complete
 #pragma unroll
-    for (int it = 0; it < 16; ++it) {
+    for (int it = 0; it < BMT / 8; ++it) {
       const int idx = it * 64 + lane;
       const int row = idx >> 3, ch = idx & 7;
       const int m = m0 + row, n = n0 + 64 * wave + 8 * ch;
@@ -272,7 +283,7 @@ __global__ __launch_bounds__(64 * WN) void gemm_large_kernel(GemmArgs a, int til
       const float b = a.bias ? load_bias(a.bias, a.bias_dtype, n) : 0.0f;
       const float c = cref[j];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < IB; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int m = m0 + 32 * i + 8 * (r >> 2) + 4 * q + (r & 3);
@@ -555,7 +566,7 @@ static bool stream_plan(int M, int N, int K, int num_cu, StreamPlan* out) {
 // The small-M kernel covers every M <= 16 with N <= 16384 * 128 (unless the
 // large-M kernel is forced).
 bool small_path(int M, int N, int K, int variant) {
-  if (variant == 1) return false;
+  if (variant == 1 || variant == 5 || variant == 6) return false;
   StreamPlan p;
   return stream_plan(M, N, K, 256, &p);
 }
@@ -589,10 +600,36 @@ static void launch_stream_t(const GemmArgs& a, const StreamPlan& p, hipStream_t 
 #undef LOWBIT_STREAM
 }
 
-// Large-M tiles: 128 x 512 (8 waves, two per SIMD) when N is wide enough,
-// else 128 x 256 (4 waves).
+// Large-M tile configurations:
+//  * wide: 128 x 512 tiles, 8 waves (two per SIMD), three stages; one
+//    workgroup fills a CU's LDS (128 x 256 and 4 waves when N < 2048);
+//  * pair: 96 x 256 tiles, 4 waves, two stages (66 KiB of LDS), so two
+//    independent workgroups share a CU: while one runs its epilogue (bias,
+//    GELU, stores) or its group-boundary rescale the other keeps the MFMA
+//    pipes busy.
+// The pair configuration is chosen when its tiles keep two workgroups on
+// every CU and its estimated time (rounds of tiles per CU slot times tile
+// area, with a 7 % bonus for the overlap, as measured on the 4608 x 9216 x
+// 3072 up-projection) beats the wide tiles' by more than 3 %.
+// variant: 5 forces wide tiles, 6 forces pair tiles.
+static bool large_pair(int M, int N, int num_cu, int variant) {
+  if (variant == 5) return false;
+  if (variant == 6) return true;
+  const int64_t tp = (int64_t)((M + 95) / 96) * ((N + 255) / 256);
+  if (N < 2048 || tp < 2 * num_cu) return false;
+  const int64_t tw = (int64_t)((M + 127) / 128) * ((N + 511) / 512);
+  const double wide = (double)((tw + num_cu - 1) / num_cu) * (128.0 * 512.0);
+  const double pair = (double)((tp + 2 * num_cu - 1) / (2 * num_cu)) * (2.0 * 96.0 * 256.0) * 0.93;
+  return pair < 0.97 * wide;
+}
+
 template <bool BF16, int FMT>
-static void launch_large_t(GemmArgs& a, hipStream_t st) {
+static void launch_large_t(const GemmArgs& a, int num_cu, int variant, hipStream_t st) {
+  if (large_pair(a.M, a.N, num_cu, variant)) {
+    const int tm = (a.M + 95) / 96, tn = (a.N + 255) / 256;
+    hipLaunchKernelGGL((gemm_large_kernel<BF16, FMT, 4, 96, 2>), dim3(tm * tn), dim3(256), 0, st, a, tm, tn);
+    return;
+  }
   const int tm = (a.M + large::BM - 1) / large::BM;
   if (a.N >= 2048) {
     const int tn = (a.N + large::bn<8>() - 1) / large::bn<8>();
@@ -604,9 +641,10 @@ static void launch_large_t(GemmArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_gemm(int fmt, bool x_bf16, GemmArgs a, int num_cu, int variant, hipStream_t st) {
-  // variant: 0 = automatic, 1 = force large-M kernel, 2 = force small-M kernel (M <= 16)
+  // variant: 0 = automatic, 1 = force the large-M kernel, 2 = force the
+  // small-M kernel (M <= 16), 5 / 6 = large-M kernel with wide / pair tiles
   StreamPlan p;
-  if (variant != 1 && stream_plan(a.M, a.N, a.K, num_cu, &p)) {
+  if (variant != 1 && variant != 5 && variant != 6 && stream_plan(a.M, a.N, a.K, num_cu, &p)) {
     if (fmt == FMT_TERNARY) {
       if (x_bf16) launch_stream_t<true, FMT_TERNARY>(a, p, st);
       else launch_stream_t<false, FMT_TERNARY>(a, p, st);
@@ -616,11 +654,11 @@ hipError_t launch_gemm(int fmt, bool x_bf16, GemmArgs a, int num_cu, int variant
     }
   } else {
     if (fmt == FMT_TERNARY) {
-      if (x_bf16) launch_large_t<true, FMT_TERNARY>(a, st);
-      else launch_large_t<false, FMT_TERNARY>(a, st);
+      if (x_bf16) launch_large_t<true, FMT_TERNARY>(a, num_cu, variant, st);
+      else launch_large_t<false, FMT_TERNARY>(a, num_cu, variant, st);
     } else {
-      if (x_bf16) launch_large_t<true, FMT_BINARY>(a, st);
-      else launch_large_t<false, FMT_BINARY>(a, st);
+      if (x_bf16) launch_large_t<true, FMT_BINARY>(a, num_cu, variant, st);
+      else launch_large_t<false, FMT_BINARY>(a, num_cu, variant, st);
     }
   }
   return hipGetLastError();

@@ -187,6 +187,29 @@ def test_small_and_large_kernels_agree_with_oracle(lb, force_variant, fmt, M, N,
         _assert_parity(Y, A, Mg, "bf16", f"{v} kernel")
 
 
+# shapes for both large-M tile configurations (128 x 512 / 128 x 256 wide
+# tiles, 96 x 256 pair tiles): ragged M and N, one or several tiles, odd
+# group counts
+_LARGE_SHAPES = [(100, 300, 1024), (257, 2100, 384), (96, 256, 128), (191, 4097, 640), (500, 1030, 1152)]
+
+
+@pytest.mark.parametrize("fmt", ["ternary", "binary"])
+@pytest.mark.parametrize("M,N,K", _LARGE_SHAPES)
+def test_large_m_tile_configurations(lb, force_variant, fmt, M, N, K):
+    lin = wl.make_linear("tiles", fmt, M, N, K, seed=520 + M, p0=0.35, with_bias=True)
+    A, Mg = oracle_linear(lin)
+    for v in ("large-wide", "large-pair"):
+        force_variant(v)
+        Y, _ = run_linear(lin)
+        _assert_parity(Y, A, Mg, "bf16", f"{v} tiles")
+    # fused GELU through the pair tiles (the epilogue runs per workgroup)
+    force_variant("large-pair")
+    Yg, _ = run_linear(lin, activation="gelu", out_dtype=torch.float32)
+    G = oracle.gelu(A)
+    lim = 1.13 * (oracle.REL_TOL * Mg + oracle.ABS_TOL) + 4 * oracle.ulp(G, "f32")
+    assert not (np.abs(Yg - G) > lim).any()
+
+
 @pytest.mark.parametrize("fmt", ["ternary", "binary"])
 @pytest.mark.parametrize("M,N,K", [(16, 3072, 9216), (3, 3072, 12288), (1, 200, 12288)])
 def test_split_k_small_m_is_deterministic_and_reusable(lb, fmt, M, N, K):
