@@ -18,7 +18,7 @@ hipError_t launch_unpack(int fmt, const uint8_t* packed, int64_t N, int64_t K, i
                          int32_t* counter, hipStream_t st);
 hipError_t launch_gemm(int fmt, bool x_bf16, GemmArgs a, int num_cu, int variant, hipStream_t st);
 hipError_t launch_gelu(const void* in, void* out, int dtype, int64_t count, hipStream_t st);
-size_t small_workspace_bytes(int M, int N, int K, int num_cu);
+size_t small_workspace_bytes(int M, int N, int K, int num_cu, int variant);
 bool small_path(int M, int N, int K, int variant);
 }  // namespace lowbit
 
@@ -65,6 +65,7 @@ int force_variant() {
   if (!std::strcmp(v, "small")) return 2;
   if (!std::strcmp(v, "large-wide")) return 5;
   if (!std::strcmp(v, "large-pair")) return 6;
+  if (!std::strcmp(v, "small-split")) return 7;
   return 0;
 }
 
@@ -148,7 +149,7 @@ size_t lowbit_gemm_workspace_bytes(int32_t format, int64_t M, int64_t N, int64_t
   int num_cu = 0;
   if (current_device(&num_cu)) return 0;
   if (!lowbit::small_path((int)M, (int)N, (int)K, force_variant())) return 0;
-  return lowbit::small_workspace_bytes((int)M, (int)N, (int)K, num_cu);
+  return lowbit::small_workspace_bytes((int)M, (int)N, (int)K, num_cu, force_variant());
 }
 
 int32_t lowbit_gemm(int32_t format, const void* X, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx,

@@ -295,9 +295,10 @@ __global__ __launch_bounds__(64 * WN) void gemm_large_kernel(GemmArgs a, int til
 
 // ===========================================================================
 // Small-M kernel (M <= 16): weight streaming with v_mfma_f32_16x16x32.
-// The grid is (column tiles) x (K splits). A workgroup of WC waves owns a
-// tile of 16 WC output columns (16 per wave) and one slice of at most GS
-// 128-groups of K:
+// The grid is (column tiles) x (K splits). A workgroup owns a tile of 16 WC
+// output columns and one slice of at most GS 128-groups of K; its WC x KH
+// waves are WC column waves (16 columns each) times KH parts of the slice
+// along K, whose FP32 results meet in LDS and are added in part order:
 //  * The activations of the slice (rows >= M repeat row M - 1: MFMA rows are
 //    independent and those outputs are never stored) go global -> LDS once
 //    per workgroup with direct LDS DMA loads, each instruction reading four
@@ -335,6 +336,12 @@ __host__ __device__ constexpr size_t lds_bytes(int gs) { return (size_t)gs * 16 
 // partials [splits][M][N]
 constexpr int MAXTILES = 16384;
 constexpr size_t TICKET_BYTES = (size_t)MAXTILES * 4;
+// K parts per workgroup: the largest KH <= 4 with WC * KH <= 16 waves and
+// whole blocks of four groups per part (GS % 4 KH == 0)
+__host__ __device__ constexpr int kparts(int wc, int gs) {
+  return (wc * 4 <= 16 && gs % 16 == 0) ? 4 : (wc * 3 <= 16 && gs % 12 == 0) ? 3
+       : (wc * 2 <= 16 && gs % 8 == 0) ? 2 : 1;
+}
 }  // namespace stream
 
 template <bool TERN>
@@ -344,19 +351,24 @@ __device__ __forceinline__ int stream_chunk(int q, int s) {
 }
 
 template <bool BF16, int FMT, int WC, int GS>
-__global__ __launch_bounds__(64 * WC) void gemm_stream_kernel(GemmArgs a, int splits, int gps) {
+__global__ __launch_bounds__(64 * WC * stream::kparts(WC, GS)) void gemm_stream_kernel(GemmArgs a, int splits, int gps) {
   constexpr bool TERN = FMT == FMT_TERNARY;
-  constexpr int NW = TERN ? GS / 2 : GS / 4;          // 16-byte code loads per lane
+  constexpr int KH = stream::kparts(WC, GS), GH = GS / KH;   // K parts, slots per part
+  constexpr int NW = TERN ? GH / 2 : (GH + 3) / 4;    // 16-byte code loads per lane
+  constexpr int NT = WC * KH;                          // waves
   extern __shared__ __align__(16) uint8_t smem[];      // [GS][16 rows][256 B] activations
+  __shared__ f32x4 red[KH][WC][64];                    // partials of the K parts
   __shared__ int last_flag;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cwv = wave % WC, kh = wave / WC;           // column wave, K part
+  const int gk0 = kh * GH;                             // first slot of this K part
   const int q = lane >> 4, c16 = lane & 15;
   const int G = a.K >> 7;
   const int tile = blockIdx.x, split = blockIdx.y;
   const int g0 = split * gps;
   const int ng = min(gps, G - g0);                      // 1 .. GS (host plan)
-  const int n = (tile * WC + wave) * 16 + c16;
+  const int n = (tile * WC + cwv) * 16 + c16;
   const int64_t nc = min(n, a.N - 1);                   // clamped: loads stay in bounds
   const int64_t wrow = TERN ? (a.K >> 2) : (a.K >> 3);
   const float factor = code_factor<TERN>();
@@ -364,8 +376,8 @@ __global__ __launch_bounds__(64 * WC) void gemm_stream_kernel(GemmArgs a, int sp
   // (1) activations of the slice -> LDS: instruction t of this wave covers
   // rows 4j .. 4j+3 of group i (slot i of the tile)
 #pragma unroll
-  for (int t = 0; t < 4 * GS / WC; ++t) {
-    const int idx = t * WC + wave;
+  for (int t = 0; t < 4 * GS / NT; ++t) {
+    const int idx = t * NT + wave;
     const int i = idx >> 2, j = idx & 3;
     if (i < ng) {                                       // wave-uniform
       const int r = 4 * j + q;                          // tile row of this lane
@@ -377,27 +389,28 @@ __global__ __launch_bounds__(64 * WC) void gemm_stream_kernel(GemmArgs a, int sp
   // activations (and a zero scale), so they add exactly zero
   {
     const int zend = min(GS, (ng + 3) & ~3);
-    for (int z = ng * 256 + tid; z < zend * 256; z += 64 * WC)
+    for (int z = ng * 256 + tid; z < zend * 256; z += 64 * NT)
       *(u32x4*)(smem + (size_t)z * 16) = u32x4{0u, 0u, 0u, 0u};
   }
-  // (2) codes: ternary load p covers groups 2p (lane groups 0, 1) and 2p+1
-  // (lane groups 2, 3); binary load p: lane group q reads group 4p + q
+  // (2) codes of this wave's K part (slots gk0 + 2p, gk0 + 2p + 1, ...):
+  // ternary load p covers slots 2p (lane groups 0, 1) and 2p+1 (lane groups
+  // 2, 3); binary load p: lane group q reads slot 4p + q
   const uint8_t* wp = a.W + nc * wrow;
   u32x4 cw[NW];
 #pragma unroll
   for (int p = 0; p < NW; ++p) {
     if (TERN) {
-      const int g = g0 + min(2 * p + (q >> 1), ng - 1);
+      const int g = g0 + min(gk0 + 2 * p + (q >> 1), ng - 1);
       cw[p] = *(const u32x4*)(wp + g * 32 + 16 * (q & 1));
     } else {
-      const int g = g0 + min(4 * p + q, ng - 1);
+      const int g = g0 + min(gk0 + 4 * p + q, ng - 1);
       cw[p] = *(const u32x4*)(wp + g * 16);
     }
   }
-  // (3) raw scales: lane group q holds groups 4j + q of its column
-  uint32_t sr[GS / 4];
+  // (3) raw scales: lane group q holds slots gk0 + 4j + q of its column
+  uint32_t sr[GH / 4];
 #pragma unroll
-  for (int j = 0; j < GS / 4; ++j) sr[j] = a.S[nc * G + g0 + min(4 * j + q, ng - 1)];
+  for (int j = 0; j < GH / 4; ++j) sr[j] = a.S[nc * G + g0 + min(gk0 + 4 * j + q, ng - 1)];
   __builtin_amdgcn_s_waitcnt(0);                        // this wave's loads and LDS DMA
   __syncthreads();                                      // everyone's LDS DMA
 
@@ -422,21 +435,21 @@ __global__ __launch_bounds__(64 * WC) void gemm_stream_kernel(GemmArgs a, int sp
   // inside a block (groups past the slice read zero activations)
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int bk = 0; bk < GS / 4; ++bk) {
-    if (4 * bk < ng) {                                  // wave-uniform
+  for (int bk = 0; bk < GH / 4; ++bk) {
+    if (gk0 + 4 * bk < ng) {                            // wave-uniform
       float sc[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int sbits = __shfl((int)sr[bk], 16 * u + c16);
-        sc[u] = 4 * bk + u < ng ? factor * half_bits_to_float((uint16_t)sbits) : 0.0f;
+        sc[u] = gk0 + 4 * bk + u < ng ? factor * half_bits_to_float((uint16_t)sbits) : 0.0f;
       }
       f32x4 tmp[4];
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const int i = 4 * bk + u;
-          const u32x4 af = *(const u32x4*)(smem + i * 4096 + c16 * 256 + ((stream_chunk<TERN>(q, s) ^ c16) << 4));
+          const int i = 4 * bk + u;                     // slot within the K part
+          const u32x4 af = *(const u32x4*)(smem + (gk0 + i) * 4096 + c16 * 256 + ((stream_chunk<TERN>(q, s) ^ c16) << 4));
           u32x4 bf;
           if (TERN) bf = tern_chunk(cw[i >> 1][(i & 1) + 2 * (s >> 1)], s & 1, TERN_MASK);
           else bf = bin_chunk(cw[i >> 2][i & 3], s, BIN_SIGN, BIN_TWO);
@@ -447,8 +460,20 @@ __global__ __launch_bounds__(64 * WC) void gemm_stream_kernel(GemmArgs a, int sp
     }
   }
 
-  // (6) output: lane holds rows 4q + e (e = 0..3) of column n
-  const bool col_ok = n < a.N;
+  // (6) the K parts meet in LDS and are added in part order (K part 0's
+  // waves go on with the sum)
+  if (KH > 1) {
+    red[kh][cwv][lane] = acc;
+    __syncthreads();
+    if (kh == 0) {
+#pragma unroll
+      for (int k2 = 1; k2 < KH; ++k2) acc += red[k2][cwv][lane];
+    }
+  }
+  const bool lead = kh == 0;
+
+  // (7) output: lane holds rows 4q + e (e = 0..3) of column n
+  const bool col_ok = n < a.N && lead;
   if (splits == 1) {
     if (col_ok) {
       const float b = a.bias ? load_bias(a.bias, a.bias_dtype, n) : 0.0f;
@@ -463,8 +488,8 @@ __global__ __launch_bounds__(64 * WC) void gemm_stream_kernel(GemmArgs a, int sp
   int* ticket = (int*)a.ws + tile;
   uint64_t* part = (uint64_t*)((uint8_t*)a.ws + stream::TICKET_BYTES);
   const int64_t tile_lanes = (int64_t)gridDim.x * WC * 64;
-  const int64_t my = (int64_t)(tile * WC + wave) * 64 + lane;
-  {
+  const int64_t my = (int64_t)(tile * WC + cwv) * 64 + lane;
+  if (lead) {
     uint64_t* dst = part + 2 * ((int64_t)split * tile_lanes + my);
     __hip_atomic_store(dst, __builtin_bit_cast(uint64_t, f32x2{acc[0], acc[1]}), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
@@ -477,7 +502,7 @@ __global__ __launch_bounds__(64 * WC) void gemm_stream_kernel(GemmArgs a, int sp
   if (tid == 0)
     last_flag = __hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == splits - 1;
   __syncthreads();
-  if (!last_flag) return;
+  if (!last_flag || !lead) return;
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   // all partial loads in flight at once, then the sum in split order
   uint64_t pv[stream::MAXSPLIT][2];
@@ -504,6 +529,156 @@ __global__ __launch_bounds__(64 * WC) void gemm_stream_kernel(GemmArgs a, int sp
   if (tid == 0) __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// ===========================================================================
+// Small-M kernel, K split inside the workgroup (M <= 16): weight streaming
+// with v_mfma_f32_16x16x32 and no cross-workgroup traffic. A workgroup owns
+// 16 CB output columns and all of K; its waves split K, wave w taking the GW
+// groups from w GW on (the last wave fewer). Per wave:
+//  * every load is issued up front: the activations of its groups go to the
+//    wave's own LDS region by direct LDS DMA (whole 256-byte group rows,
+//    chunks XOR-swizzled by row as in the kernel above; rows >= M repeat row
+//    M - 1, whose outputs are never stored), so only the wave's own wait is
+//    needed before it reads them; the codes of each column block come as
+//    16-byte loads covering two groups (ternary) or one group (binary) per
+//    lane, exchanged with v_permlane32_swap / v_permlane16_swap exactly as
+//    in the kernel above, and the raw scales;
+//  * four groups at a time run as four chained MFMAs each, then
+//    acc += (scale * factor) * tmp; groups past the wave's share get a zero
+//    scale.
+// The FP32 partial tiles of the waves meet in LDS and are added in wave
+// order (deterministic); bias, activation, one RNE cast and the stores
+// follow. With no split across workgroups there is no workspace and no
+// global atomic, and with a K split inside each workgroup there are enough
+// waves in flight even when N / 16 is below the CU count.
+// ===========================================================================
+namespace thin {
+constexpr int MAXWAVES = 16;                   // 1024 threads, at most 128 VGPRs (GW <= 4)
+}
+
+template <bool BF16, int FMT, int GW, int CB>
+__global__ __launch_bounds__(64 * thin::MAXWAVES) void gemm_thin_kernel(GemmArgs a) {
+  static_assert(GW <= 4, "at most four groups per wave at 16 waves");
+  constexpr bool TERN = FMT == FMT_TERNARY;
+  constexpr int NW = TERN ? (GW + 1) / 2 : (GW + 3) / 4;   // 16-byte code loads per lane and column block
+  constexpr int NB = (GW + 3) / 4;                          // blocks of four groups
+  extern __shared__ __align__(16) uint8_t smem[];          // [waves][GW][16 rows][256 B] activations
+  __shared__ f32x4 red[thin::MAXWAVES][CB][64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nwav = blockDim.x >> 6;
+  const int q = lane >> 4, c16 = lane & 15;
+  const int G = a.K >> 7;
+  const int g0 = wave * GW;
+  const int ng = min(GW, G - g0);                           // 1 .. GW (host plan)
+  const int64_t wrow = TERN ? (a.K >> 2) : (a.K >> 3);
+  const float factor = code_factor<TERN>();
+  const int col0 = blockIdx.x * 16 * CB;
+
+  // (1) activations of the wave's groups -> the wave's own LDS region by
+  // direct LDS DMA, four whole 256-byte group rows per instruction; slot i
+  // holds group g0 + min(i, ng - 1), 16-byte chunks XOR-swizzled by row
+  uint8_t* xs = smem + (size_t)wave * GW * 4096;
+#pragma unroll
+  for (int i = 0; i < GW; ++i) {
+    const int gi = g0 + min(i, ng - 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 4 * j + q;                              // row of this lane
+      const uint16_t* src = a.X + (int64_t)min(r, a.M - 1) * a.ldx + (gi << 7) + 8 * ((c16 ^ r) & 15);
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr_t)(xs + i * 4096 + j * 1024), 16, 0, 0);
+    }
+  }
+  // (2) codes and raw scales of each column block (columns past N: any
+  // valid column; groups past the share: the last one of the share)
+  u32x4 cw[CB][NW];
+  uint32_t sr[CB][NB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    const int64_t nc = min(col0 + 16 * cb + c16, a.N - 1);
+    const uint8_t* wp = a.W + nc * wrow;
+#pragma unroll
+    for (int p = 0; p < NW; ++p) {
+      if (TERN) {
+        const int g = g0 + min(2 * p + (q >> 1), ng - 1);
+        cw[cb][p] = *(const u32x4*)(wp + g * 32 + 16 * (q & 1));
+      } else {
+        const int g = g0 + min(4 * p + q, ng - 1);
+        cw[cb][p] = *(const u32x4*)(wp + g * 16);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NB; ++j) sr[cb][j] = a.S[nc * G + g0 + min(4 * j + q, ng - 1)];
+  }
+
+  __builtin_amdgcn_s_waitcnt(0);                            // this wave's loads and LDS DMA
+
+  f32x4 acc[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    // (3) lane exchange (as in the kernel above)
+#pragma unroll
+    for (int p = 0; p < NW; ++p) {
+      if (TERN) {
+        auto x = __builtin_amdgcn_permlane32_swap(cw[cb][p][0], cw[cb][p][1], false, false);
+        auto y = __builtin_amdgcn_permlane32_swap(cw[cb][p][2], cw[cb][p][3], false, false);
+        cw[cb][p] = u32x4{x[0], x[1], y[0], y[1]};
+      } else {
+        auto x = __builtin_amdgcn_permlane32_swap(cw[cb][p][0], cw[cb][p][2], false, false);
+        auto y = __builtin_amdgcn_permlane32_swap(cw[cb][p][1], cw[cb][p][3], false, false);
+        auto u = __builtin_amdgcn_permlane16_swap(x[0], y[0], false, false);
+        auto v = __builtin_amdgcn_permlane16_swap(x[1], y[1], false, false);
+        cw[cb][p] = u32x4{u[0], u[1], v[0], v[1]};
+      }
+    }
+    // (4) MFMAs, four groups at a time
+    acc[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int bk = 0; bk < NB; ++bk) {
+      if (4 * bk < ng) {                                    // wave-uniform
+        float sc[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int sbits = __shfl((int)sr[cb][bk], 16 * u + c16);
+          sc[u] = 4 * bk + u < ng ? factor * half_bits_to_float((uint16_t)sbits) : 0.0f;
+        }
+        f32x4 tmp[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int i = 4 * bk + u;
+            if (i < GW) {
+              u32x4 bf;
+              if (TERN) bf = tern_chunk(cw[cb][i >> 1][(i & 1) + 2 * (s >> 1)], s & 1, TERN_MASK);
+              else bf = bin_chunk(cw[cb][i >> 2][i & 3], s, BIN_SIGN, BIN_TWO);
+              const u32x4 af = *(const u32x4*)(xs + i * 4096 + c16 * 256 + ((stream_chunk<TERN>(q, s) ^ c16) << 4));
+              tmp[u] = mfma16<BF16>(af, bf, s == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : tmp[u]);
+            }
+          }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (4 * bk + u < GW) acc[cb] += sc[u] * tmp[u];
+      }
+    }
+    red[wave][cb][lane] = acc[cb];
+  }
+  __syncthreads();
+
+  // (5) sum of the waves' partials in wave order, epilogue; lane holds rows
+  // 4q + e (e = 0..3) of column n
+  for (int cb = wave; cb < CB; cb += nwav) {
+    f32x4 sum = red[0][cb][lane];
+    for (int w = 1; w < nwav; ++w) sum += red[w][cb][lane];
+    const int n = col0 + 16 * cb + c16;
+    if (n < a.N) {
+      const float b = a.bias ? load_bias(a.bias, a.bias_dtype, n) : 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (4 * q + e < a.M) store_out(a.Y, a.ldy, a.y_dtype, 4 * q + e, n, finish(sum[e], b, a.act));
+    }
+  }
+}
+
 // Standalone exact-erf GELU.
 __global__ void gelu_kernel(const void* in, void* out, int dtype, int64_t count) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
@@ -523,10 +698,30 @@ __global__ void gelu_kernel(const void* in, void* out, int dtype, int64_t count)
 // Host-side launch helpers
 // ===========================================================================
 
-// Small-M plan: tiles of 64 columns (4 waves), or 128 (8 waves) when that
+// Plan of the small-M kernel with the K split inside the workgroup: one
+// 16-column block per workgroup (CB = 1), GW groups per wave. It is used
+// only while N / 16 is below the CU count: every workgroup reads all of X
+// from L2, and for wider N the kernel above (X shared through LDS by 64 or
+// 128 columns) is faster. GW is 2, or 4 when 2 would need more than 16
+// waves; the activations of the whole K range sit in LDS, so K <= 4608.
+struct ThinPlan { int gw, cb, waves, blocks; };
+
+static bool thin_plan(int M, int N, int K, int num_cu, ThinPlan* out) {
+  if (M > 16 || (N + 15) / 16 >= num_cu) return false;
+  const int G = K / 128;
+  const int gw = (G + 1) / 2 <= thin::MAXWAVES ? 2 : 4;
+  const int waves = (G + gw - 1) / gw;
+  if (waves > thin::MAXWAVES || (size_t)waves * gw * 4096 + 16 * 1024 > 160 * 1024)
+    return false;                                       // activations + partials in LDS
+  *out = ThinPlan{gw, 1, waves, (N + 15) / 16};
+  return true;
+}
+
+// Small-M plan: tiles of 64 columns (4 column waves), or 128 (8) when that
 // still gives at least 128 tiles; then the K split S (1 .. MAXSPLIT, at most
 // MAXGS groups per slice) that minimises a rough time estimate:
-//   rounds * (slice bytes through one CU at ~64 B/clk + slice MFMA work)
+//   rounds * (slice bytes through one CU at ~64 B/clk + slice MFMA work
+//   shared by the slice's K parts)
 //   + a fixed cost for the cross-workgroup combine when S > 1
 // (the combine waits for written partials, a ticket and the read-back, each
 // a memory round trip). The compiled slice size GS is gps rounded up to a
@@ -549,10 +744,11 @@ static bool stream_plan(int M, int N, int K, int num_cu, StreamPlan* out) {
     if (gps > stream::MAXGS) continue;
     const int S = (G + gps - 1) / gps;
     const int gs = round_gs(gps);
-    const size_t lds = stream::lds_bytes(gs);
-    const int per_cu = max(1, min((int)(160 * 1024 / lds), 32 / wc));
+    const int kh = stream::kparts(wc, gs);
+    const size_t lds = stream::lds_bytes(gs) + (size_t)kh * wc * 1024;
+    const int per_cu = max(1, min((int)(160 * 1024 / lds), 32 / (wc * kh)));
     const int rounds = (tiles * S + num_cu * per_cu - 1) / (num_cu * per_cu);
-    const double clk = gps * (4096.0 + wc * 16 * 32) / 64.0 + gps * 4 * 40.0;
+    const double clk = gps * (4096.0 + wc * 16 * 32) / 64.0 + gps * 4 * 40.0 / kh;
     const double us = rounds * clk / 2100.0 + (S > 1 ? 3.0 : 0.0);
     if (us < best) {
       best = us;
@@ -568,19 +764,30 @@ static bool stream_plan(int M, int N, int K, int num_cu, StreamPlan* out) {
 bool small_path(int M, int N, int K, int variant) {
   if (variant == 1 || variant == 5 || variant == 6) return false;
   StreamPlan p;
-  return stream_plan(M, N, K, 256, &p);
+  ThinPlan tp;
+  return (variant != 7 && thin_plan(M, N, K, 256, &tp)) || stream_plan(M, N, K, 256, &p);
 }
 
 // Workspace of the small-M kernel when K is split: partials and tickets.
-size_t small_workspace_bytes(int M, int N, int K, int num_cu) {
+size_t small_workspace_bytes(int M, int N, int K, int num_cu, int variant) {
+  ThinPlan tp;
+  if (variant != 7 && thin_plan(M, N, K, num_cu, &tp)) return 0;
   StreamPlan p;
   if (!stream_plan(M, N, K, num_cu, &p) || p.splits == 1) return 0;
   return stream::TICKET_BYTES + (size_t)p.splits * p.tiles * p.wc * 64 * 4 * sizeof(float);
 }
 
 template <bool BF16, int FMT>
+static void launch_thin_t(const GemmArgs& a, const ThinPlan& p, hipStream_t st) {
+  const dim3 grid(p.blocks), block(64 * p.waves);
+  const size_t lds = (size_t)p.waves * p.gw * 4096;
+  if (p.gw == 2) hipLaunchKernelGGL((gemm_thin_kernel<BF16, FMT, 2, 1>), grid, block, lds, st, a);
+  else hipLaunchKernelGGL((gemm_thin_kernel<BF16, FMT, 4, 1>), grid, block, lds, st, a);
+}
+
+template <bool BF16, int FMT>
 static void launch_stream_t(const GemmArgs& a, const StreamPlan& p, hipStream_t st) {
-  const dim3 grid(p.tiles, p.splits), block(64 * p.wc);
+  const dim3 grid(p.tiles, p.splits), block(64 * p.wc * stream::kparts(p.wc, p.gs));
   const size_t lds = stream::lds_bytes(p.gs);
 #define LOWBIT_STREAM(WC, GS) \
   hipLaunchKernelGGL((gemm_stream_kernel<BF16, FMT, WC, GS>), grid, block, lds, st, a, p.splits, p.gps)
@@ -641,10 +848,20 @@ static void launch_large_t(const GemmArgs& a, int num_cu, int variant, hipStream
 }
 
 hipError_t launch_gemm(int fmt, bool x_bf16, GemmArgs a, int num_cu, int variant, hipStream_t st) {
-  // variant: 0 = automatic, 1 = force the large-M kernel, 2 = force the
-  // small-M kernel (M <= 16), 5 / 6 = large-M kernel with wide / pair tiles
+  // variant: 0 = automatic, 1 = force the large-M kernel, 2 = small-M
+  // kernels only (M <= 16), 5 / 6 = large-M kernel with wide / pair tiles,
+  // 7 = the small-M kernel with the K split across workgroups
   StreamPlan p;
-  if (variant != 1 && variant != 5 && variant != 6 && stream_plan(a.M, a.N, a.K, num_cu, &p)) {
+  ThinPlan tp;
+  if (variant != 1 && variant != 5 && variant != 6 && variant != 7 && thin_plan(a.M, a.N, a.K, num_cu, &tp)) {
+    if (fmt == FMT_TERNARY) {
+      if (x_bf16) launch_thin_t<true, FMT_TERNARY>(a, tp, st);
+      else launch_thin_t<false, FMT_TERNARY>(a, tp, st);
+    } else {
+      if (x_bf16) launch_thin_t<true, FMT_BINARY>(a, tp, st);
+      else launch_thin_t<false, FMT_BINARY>(a, tp, st);
+    }
+  } else if (variant != 1 && variant != 5 && variant != 6 && stream_plan(a.M, a.N, a.K, num_cu, &p)) {
     if (fmt == FMT_TERNARY) {
       if (x_bf16) launch_stream_t<true, FMT_TERNARY>(a, p, st);
       else launch_stream_t<false, FMT_TERNARY>(a, p, st);

@@ -168,12 +168,15 @@ def test_special_scales_and_codes(lb):
 
 # ---------------------------------------------------- variants / safety ---
 
-# shapes that reach every compiled variant of the small-M kernel: 4- and
-# 8-wave tiles, slices of 4 .. 32 groups, one or many K splits, odd group
-# counts, ragged N, M < 16
+# shapes that reach every compiled variant of the two small-M kernels: the
+# one with the K split inside the workgroup (N / 16 below the CU count, K up
+# to 4608; 2, 4 or 8 groups per wave) and the one with column tiles of 64 or
+# 128, slices of 4 .. 32 groups split into K parts, one or many K splits;
+# odd group counts, ragged N, M < 16
 _SMALL_SHAPES = [(5, 64, 512), (16, 3072, 3072), (7, 520, 6144), (1, 200, 12288),
                  (16, 8192, 1024), (3, 8200, 2048), (16, 18432, 3072), (2, 8192, 8192),
-                 (16, 100, 16384), (16, 100, 4096), (9, 3000, 2560)]
+                 (16, 100, 16384), (16, 100, 4096), (9, 3000, 2560), (16, 1000, 4608),
+                 (4, 4000, 128), (13, 2048, 1152)]
 
 
 @pytest.mark.parametrize("fmt", ["ternary", "binary"])
@@ -181,7 +184,7 @@ _SMALL_SHAPES = [(5, 64, 512), (16, 3072, 3072), (7, 520, 6144), (1, 200, 12288)
 def test_small_and_large_kernels_agree_with_oracle(lb, force_variant, fmt, M, N, K):
     lin = wl.make_linear("both", fmt, M, N, K, seed=500 + M, p0=0.35)
     A, Mg = oracle_linear(lin)
-    for v in ("small", "large"):
+    for v in ("small", "small-split", "large"):
         force_variant(v)
         Y, _ = run_linear(lin)
         _assert_parity(Y, A, Mg, "bf16", f"{v} kernel")
