@@ -193,6 +193,84 @@ def traffic_probe(torch, lb):
     print("traffic probe done", flush=True)
 
 
+def traffic_summary(fetch_csv: str, write_csv: str) -> dict:
+    """Write TRAFFIC_FILE from the two rocprofv3 --pmc counter files of the
+    --traffic-probe workload (FETCH_SIZE run, WRITE_SIZE run). The counters
+    are scaled by what they read for the calibration copy (the largest
+    __amd_rocclr_copyBuffer dispatch: 256 MiB read and written); the GEMM
+    launches are told apart by grid size (up-projection, down-projection)."""
+    import csv
+
+    def read(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        calib = max(float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"])
+        gemm = {}
+        for r in rows:
+            if "gemm_large_kernel" in r["Kernel_Name"]:
+                gemm.setdefault(int(r["Grid_Size"]), (r["Kernel_Name"], []))[1].append(float(r["Counter_Value"]))
+        return calib, gemm
+
+    copy_kib = (256 << 20) / 1024
+    f_cal, f_gemm = read(fetch_csv, "FETCH_SIZE")
+    w_cal, w_gemm = read(write_csv, "WRITE_SIZE")
+    ff, wf = copy_kib / f_cal, copy_kib / w_cal
+    import workloads as wl
+    up, down = wl.config3()
+    alg = {name: lin.N * lin.K // 4 + lin.N * lin.K // 64 + 2 * lin.M * lin.K + 2 * lin.M * lin.N
+           for name, lin in (("up", up), ("down", down))}
+    out = {
+        "kernel": "gemm_large_kernel<bf16, ternary>",
+        "workload": "MLP pair of a 1024x1024 step: up 4608x9216x3072 (+GELU), down 4608x3072x9216, "
+                    "bf16, ternary, group 128",
+        "kernel_source_sha": kernel_source_sha(),
+        "kernel_source_sha_note": "sha256 of gemm.hip + common.h with // comments and blank lines removed "
+                                  "(bench.py kernel_source_sha)",
+        "how": "hbm_bytes = (FETCH_SIZE_KiB * fetch_factor + WRITE_SIZE_KiB * write_factor) * 1024, mean over "
+               "dispatches; factors = 262144 KiB / the counter value of a plain 256 MiB device copy",
+        "calibration": {"copy_bytes": 256 << 20, "fetch_kib": f_cal, "write_kib": w_cal,
+                        "fetch_factor": round(ff, 4), "write_factor": round(wf, 4)},
+    }
+    # the up-projection has the larger grid (more, smaller tiles or more rows of tiles)
+    grids = sorted(f_gemm, reverse=True)
+    if len(grids) != 2 or sorted(w_gemm, reverse=True) != grids:
+        raise SystemExit(f"expected two GEMM launch shapes, found grids {grids}")
+    total = 0.0
+    for name, g in zip(("up", "down"), grids):
+        fk = float(np.mean(f_gemm[g][1]))
+        wk = float(np.mean(w_gemm[g][1]))
+        hb = (fk * ff + wk * wf) * 1024
+        total += hb
+        out[name] = {"kernel_name": f_gemm[g][0], "grid": g, "dispatches": len(f_gemm[g][1]),
+                     "fetch_kib": fk, "write_kib": wk, "hbm_bytes": int(round(hb)),
+                     "algorithmic_bytes": int(alg[name])}
+    out["bytes_per_launch"] = int(round(total / 2))
+    out["commands"] = [
+        "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv "
+        "-d $REPO/gpurun_out/tr_FETCH_SIZE -o run -- python $REPO/bench.py --traffic-probe",
+        "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv "
+        "-d $REPO/gpurun_out/tr_WRITE_SIZE -o run -- python $REPO/bench.py --traffic-probe",
+        "python bench.py --traffic-summary $REPO/gpurun_out/tr_FETCH_SIZE/run_counter_collection.csv "
+        "$REPO/gpurun_out/tr_WRITE_SIZE/run_counter_collection.csv",
+    ]
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=2)
+        f.write("\n")
+    return out
+
+
+def stats_table(stats_csv: str, limit: int = 12) -> str:
+    """Markdown table of a rocprofv3 --kernel-trace --stats kernel_stats.csv
+    (durations converted from ns to us)."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    out = ["| kernel | calls | total us | average us | min us | max us | % |", "|---|---|---|---|---|---|---|"]
+    for r in rows[:limit]:
+        out.append("| `{}` | {} | {:.1f} | {:.1f} | {:.1f} | {:.1f} | {:.2f} |".format(
+            r["Name"][:110], r["Calls"], float(r["TotalDurationNs"]) / 1e3, float(r["AverageNs"]) / 1e3,
+            float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    return "\n".join(out)
+
+
 def cpu_baseline(seconds_target=10.0):
     """The oracle as it stands (float64 dequantise + BLAS matmul) on a bounded
     sample of the step: the first R rows of the MLP pair (R grown up to all 4608),
@@ -236,7 +314,17 @@ def main():
     ap.add_argument("--no-small", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run the counter-calibration workload instead of the benchmark")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the HBM traffic summary from the two counter runs and exit")
+    ap.add_argument("--stats-table", metavar="STATS_CSV",
+                    help="print a rocprofv3 kernel_stats.csv as a markdown table and exit")
     args = ap.parse_args()
+    if args.traffic_summary:
+        print(json.dumps(traffic_summary(*args.traffic_summary)))
+        return
+    if args.stats_table:
+        print(stats_table(args.stats_table))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the low-bit linear layer runs on a single "
               "device here; run with --gpus 1", file=sys.stderr)
@@ -286,7 +374,8 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": "gemm_large_kernel<bf16, ternary>",
+            "kernel": "gemm_large_kernel<bf16, ternary>, mean of its two launches per step "
+                      "(up: 96x256 tiles, two workgroups per CU; down: 128x512 tiles)",
             "avg_launch_ms": round(r["avg_launch_ms"], 4),
             "flop_per_launch": r["flop_launch"],
         },
