@@ -258,6 +258,41 @@ def traffic_summary(fetch_csv: str, write_csv: str) -> dict:
     return out
 
 
+def counter_table(csvs, num_simd: int = 1024, num_xcd: int = 8) -> str:
+    """Markdown table of per-kernel means of the rocprofv3 --pmc counters in
+    the given counter_collection.csv files (one row per kernel name and grid
+    size), with MFMA utilisation = SQ_VALU_MFMA_BUSY_CYCLES (summed over all
+    SIMDs) / (GRBM_GUI_ACTIVE / XCDs x SIMDs) -- GRBM_GUI_ACTIVE reads as the
+    sum over the 8 XCDs -- and VALU instructions per MFMA where those
+    counters are there."""
+    import csv
+    agg = {}
+    for path in csvs:
+        for r in csv.DictReader(open(path)):
+            name = r["Kernel_Name"]
+            if "lowbit::gemm" not in name:
+                continue
+            key = (name.split("(")[0].replace("void ", ""), int(r["Grid_Size"]))
+            agg.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    cols = sorted({c for d in agg.values() for c in d})
+    head = ["kernel", "grid", "dispatches"] + cols
+    derived = []
+    if {"SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"} <= set(cols):
+        derived.append("MFMA busy %")
+    if {"SQ_INSTS_VALU", "SQ_INSTS_MFMA"} <= set(cols):
+        derived.append("VALU per MFMA")
+    out = ["| " + " | ".join(head + derived) + " |", "|" + "---|" * (len(head) + len(derived))]
+    for (name, grid), d in sorted(agg.items(), key=lambda kv: -len(next(iter(kv[1].values())))):
+        m = {c: float(np.mean(v)) for c, v in d.items()}
+        row = [f"`{name}`", str(grid), str(len(next(iter(d.values()))))] + [f"{m[c]:.4g}" if c in m else "" for c in cols]
+        if "MFMA busy %" in derived:
+            row.append(f"{100 * m['SQ_VALU_MFMA_BUSY_CYCLES'] / (m['GRBM_GUI_ACTIVE'] / num_xcd * num_simd):.1f}")
+        if "VALU per MFMA" in derived:
+            row.append(f"{(m['SQ_INSTS_VALU'] - m['SQ_INSTS_MFMA']) / max(m['SQ_INSTS_MFMA'], 1):.2f}")
+        out.append("| " + " | ".join(row) + " |")
+    return "\n".join(out)
+
+
 def stats_table(stats_csv: str, limit: int = 12) -> str:
     """Markdown table of a rocprofv3 --kernel-trace --stats kernel_stats.csv
     (durations converted from ns to us)."""
@@ -318,7 +353,12 @@ def main():
                     help="write the HBM traffic summary from the two counter runs and exit")
     ap.add_argument("--stats-table", metavar="STATS_CSV",
                     help="print a rocprofv3 kernel_stats.csv as a markdown table and exit")
+    ap.add_argument("--counter-table", nargs="+", metavar="COUNTER_CSV",
+                    help="print per-kernel means of rocprofv3 --pmc counter files and exit")
     args = ap.parse_args()
+    if args.counter_table:
+        print(counter_table(args.counter_table))
+        return
     if args.traffic_summary:
         print(json.dumps(traffic_summary(*args.traffic_summary)))
         return
