@@ -532,19 +532,24 @@ __global__ __launch_bounds__(64 * WC * stream::kparts(WC, GS)) void gemm_stream_
 // ===========================================================================
 // Small-M kernel, K split inside the workgroup (M <= 16): weight streaming
 // with v_mfma_f32_16x16x32 and no cross-workgroup traffic. A workgroup owns
-// 16 CB output columns and all of K; its waves split K, wave w taking the GW
-// groups from w GW on (the last wave fewer). Per wave:
-//  * every load is issued up front: the activations of its groups go to the
-//    wave's own LDS region by direct LDS DMA (whole 256-byte group rows,
-//    chunks XOR-swizzled by row as in the kernel above; rows >= M repeat row
-//    M - 1, whose outputs are never stored), so only the wave's own wait is
-//    needed before it reads them; the codes of each column block come as
-//    16-byte loads covering two groups (ternary) or one group (binary) per
-//    lane, exchanged with v_permlane32_swap / v_permlane16_swap exactly as
-//    in the kernel above, and the raw scales;
-//  * four groups at a time run as four chained MFMAs each, then
-//    acc += (scale * factor) * tmp; groups past the wave's share get a zero
-//    scale.
+// 16 output columns and all of K; its waves split K, wave w taking the
+// GW * NCH groups from w GW NCH on (the last wave fewer), in NCH chunks of
+// GW groups. Per wave and chunk:
+//  * the activations of the chunk's groups go to the wave's own LDS region
+//    by direct LDS DMA (whole 256-byte group rows, chunks XOR-swizzled by
+//    row as in the kernel above; rows >= M repeat row M - 1, whose outputs
+//    are never stored), so only the wave's own wait is needed before it
+//    reads them; the codes come as 16-byte loads covering two groups
+//    (ternary) or one group (binary) per lane, exchanged with
+//    v_permlane32_swap / v_permlane16_swap exactly as in the kernel above;
+//    then the raw scales. Groups past the wave's share load the share's last
+//    group again and get a zero scale, so every chunk issues the same loads;
+//  * the groups run as chained MFMAs (four per group), then
+//    acc += (scale * factor) * tmp.
+// With one chunk every load is issued up front. With more, chunks c and c+1
+// are in flight in two LDS buffers and two register sets: the wave waits
+// for chunk c only (the loads of chunk c+1 may still be outstanding),
+// computes it, and then issues chunk c+2 into the buffers chunk c used.
 // The FP32 partial tiles of the waves meet in LDS and are added in wave
 // order (deterministic); bias, activation, one RNE cast and the stores
 // follow. With no split across workgroups there is no workspace and no
@@ -552,124 +557,126 @@ __global__ __launch_bounds__(64 * WC * stream::kparts(WC, GS)) void gemm_stream_
 // waves in flight even when N / 16 is below the CU count.
 // ===========================================================================
 namespace thin {
-constexpr int MAXWAVES = 16;                   // 1024 threads, at most 128 VGPRs (GW <= 4)
+constexpr int MAXWAVES = 16;                   // one chunk: 1024 threads, at most 128 VGPRs
+constexpr int MAXWAVES_CHUNKED = 8;            // several chunks: 512 threads
 }
 
-template <bool BF16, int FMT, int GW, int CB>
-__global__ __launch_bounds__(64 * thin::MAXWAVES) void gemm_thin_kernel(GemmArgs a) {
-  static_assert(GW <= 4, "at most four groups per wave at 16 waves");
+template <bool BF16, int FMT, int GW, int NCH>
+__global__ __launch_bounds__(64 * (NCH == 1 ? thin::MAXWAVES : thin::MAXWAVES_CHUNKED)) void gemm_thin_kernel(GemmArgs a) {
+  static_assert(GW == 2 || GW == 4, "two or four groups per chunk");
   constexpr bool TERN = FMT == FMT_TERNARY;
-  constexpr int NW = TERN ? (GW + 1) / 2 : (GW + 3) / 4;   // 16-byte code loads per lane and column block
-  constexpr int NB = (GW + 3) / 4;                          // blocks of four groups
-  extern __shared__ __align__(16) uint8_t smem[];          // [waves][GW][16 rows][256 B] activations
-  __shared__ f32x4 red[thin::MAXWAVES][CB][64];
+  constexpr int NW = TERN ? GW / 2 : 1;                     // 16-byte code loads per lane and chunk
+  constexpr int NBUF = NCH == 1 ? 1 : 2;                    // chunk buffers in flight
+  // activation DMA instructions per chunk. Waiting until at most this many
+  // loads are outstanding guarantees chunk c's DMAs have landed once chunk
+  // c+1's DMAs (issued after them, in order) are the only ones that may
+  // still be in flight, wherever the compiler places the register loads.
+  constexpr int XDMA = 4 * GW;
+  extern __shared__ __align__(16) uint8_t smem[];          // [waves][NBUF][GW][16 rows][256 B] activations
+  __shared__ f32x4 red[NCH == 1 ? thin::MAXWAVES : thin::MAXWAVES_CHUNKED][64];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nwav = blockDim.x >> 6;
   const int q = lane >> 4, c16 = lane & 15;
   const int G = a.K >> 7;
-  const int g0 = wave * GW;
-  const int ng = min(GW, G - g0);                           // 1 .. GW (host plan)
+  const int g0 = wave * GW * NCH;
+  const int ng = min(GW * NCH, G - g0);                     // 1 .. GW NCH (host plan)
   const int64_t wrow = TERN ? (a.K >> 2) : (a.K >> 3);
   const float factor = code_factor<TERN>();
-  const int col0 = blockIdx.x * 16 * CB;
+  const int n = blockIdx.x * 16 + c16;
+  const int64_t nc = min(n, a.N - 1);                       // columns past N: any valid column
+  const uint8_t* wp = a.W + nc * wrow;
+  uint8_t* xw = smem + (size_t)wave * NBUF * GW * 4096;
 
-  // (1) activations of the wave's groups -> the wave's own LDS region by
-  // direct LDS DMA, four whole 256-byte group rows per instruction; slot i
-  // holds group g0 + min(i, ng - 1), 16-byte chunks XOR-swizzled by row
-  uint8_t* xs = smem + (size_t)wave * GW * 4096;
+  u32x4 cw[NBUF][NW];
+  uint32_t sr[NBUF];
+  // issue the loads of chunk c into buffer / register set c % NBUF
+  auto issue = [&](int c) __attribute__((always_inline)) {
+    const int bsel = c % NBUF;
+    uint8_t* xs = xw + bsel * GW * 4096;
 #pragma unroll
-  for (int i = 0; i < GW; ++i) {
-    const int gi = g0 + min(i, ng - 1);
+    for (int i = 0; i < GW; ++i) {
+      const int gi = g0 + min(c * GW + i, ng - 1);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = 4 * j + q;                              // row of this lane
-      const uint16_t* src = a.X + (int64_t)min(r, a.M - 1) * a.ldx + (gi << 7) + 8 * ((c16 ^ r) & 15);
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr_t)(xs + i * 4096 + j * 1024), 16, 0, 0);
-    }
-  }
-  // (2) codes and raw scales of each column block (columns past N: any
-  // valid column; groups past the share: the last one of the share)
-  u32x4 cw[CB][NW];
-  uint32_t sr[CB][NB];
-#pragma unroll
-  for (int cb = 0; cb < CB; ++cb) {
-    const int64_t nc = min(col0 + 16 * cb + c16, a.N - 1);
-    const uint8_t* wp = a.W + nc * wrow;
-#pragma unroll
-    for (int p = 0; p < NW; ++p) {
-      if (TERN) {
-        const int g = g0 + min(2 * p + (q >> 1), ng - 1);
-        cw[cb][p] = *(const u32x4*)(wp + g * 32 + 16 * (q & 1));
-      } else {
-        const int g = g0 + min(4 * p + q, ng - 1);
-        cw[cb][p] = *(const u32x4*)(wp + g * 16);
+      for (int j = 0; j < 4; ++j) {
+        const int r = 4 * j + q;                            // row of this lane
+        const uint16_t* src = a.X + (int64_t)min(r, a.M - 1) * a.ldx + (gi << 7) + 8 * ((c16 ^ r) & 15);
+        __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr_t)(xs + i * 4096 + j * 1024), 16, 0, 0);
       }
     }
 #pragma unroll
-    for (int j = 0; j < NB; ++j) sr[cb][j] = a.S[nc * G + g0 + min(4 * j + q, ng - 1)];
-  }
-
-  __builtin_amdgcn_s_waitcnt(0);                            // this wave's loads and LDS DMA
-
-  f32x4 acc[CB];
-#pragma unroll
-  for (int cb = 0; cb < CB; ++cb) {
-    // (3) lane exchange (as in the kernel above)
-#pragma unroll
     for (int p = 0; p < NW; ++p) {
       if (TERN) {
-        auto x = __builtin_amdgcn_permlane32_swap(cw[cb][p][0], cw[cb][p][1], false, false);
-        auto y = __builtin_amdgcn_permlane32_swap(cw[cb][p][2], cw[cb][p][3], false, false);
-        cw[cb][p] = u32x4{x[0], x[1], y[0], y[1]};
+        const int g = g0 + min(c * GW + 2 * p + (q >> 1), ng - 1);
+        cw[bsel][p] = *(const u32x4*)(wp + g * 32 + 16 * (q & 1));
       } else {
-        auto x = __builtin_amdgcn_permlane32_swap(cw[cb][p][0], cw[cb][p][2], false, false);
-        auto y = __builtin_amdgcn_permlane32_swap(cw[cb][p][1], cw[cb][p][3], false, false);
-        auto u = __builtin_amdgcn_permlane16_swap(x[0], y[0], false, false);
-        auto v = __builtin_amdgcn_permlane16_swap(x[1], y[1], false, false);
-        cw[cb][p] = u32x4{u[0], u[1], v[0], v[1]};
+        const int g = g0 + min(c * GW + q, ng - 1);
+        cw[bsel][p] = *(const u32x4*)(wp + g * 16);
       }
     }
-    // (4) MFMAs, four groups at a time
-    acc[cb] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    sr[bsel] = a.S[nc * G + g0 + min(c * GW + q, ng - 1)];  // lane group q: group c GW + q
+    asm volatile("" ::: "memory");                          // keep the chunks' loads in order
+  };
+
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  issue(0);
+  if (NCH > 1) issue(1);
 #pragma unroll
-    for (int bk = 0; bk < NB; ++bk) {
-      if (4 * bk < ng) {                                    // wave-uniform
-        float sc[4];
+  for (int c = 0; c < NCH; ++c) {
+    const int bsel = c % NBUF;
+    // chunk c has landed (the loads of chunk c+1 may still be in flight)
+    if (c + 1 < NCH) __builtin_amdgcn_s_waitcnt(large::waitcnt_vm(XDMA));
+    else __builtin_amdgcn_s_waitcnt(0);
+    if (c * GW < ng) {                                      // wave-uniform
+      // lane exchange (as in the kernel above)
+      u32x4 w[NW];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int sbits = __shfl((int)sr[cb][bk], 16 * u + c16);
-          sc[u] = 4 * bk + u < ng ? factor * half_bits_to_float((uint16_t)sbits) : 0.0f;
+      for (int p = 0; p < NW; ++p) {
+        if (TERN) {
+          auto x = __builtin_amdgcn_permlane32_swap(cw[bsel][p][0], cw[bsel][p][1], false, false);
+          auto y = __builtin_amdgcn_permlane32_swap(cw[bsel][p][2], cw[bsel][p][3], false, false);
+          w[p] = u32x4{x[0], x[1], y[0], y[1]};
+        } else {
+          auto x = __builtin_amdgcn_permlane32_swap(cw[bsel][p][0], cw[bsel][p][2], false, false);
+          auto y = __builtin_amdgcn_permlane32_swap(cw[bsel][p][1], cw[bsel][p][3], false, false);
+          auto u = __builtin_amdgcn_permlane16_swap(x[0], y[0], false, false);
+          auto v = __builtin_amdgcn_permlane16_swap(x[1], y[1], false, false);
+          w[p] = u32x4{u[0], u[1], v[0], v[1]};
         }
-        f32x4 tmp[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const int i = 4 * bk + u;
-            if (i < GW) {
-              u32x4 bf;
-              if (TERN) bf = tern_chunk(cw[cb][i >> 1][(i & 1) + 2 * (s >> 1)], s & 1, TERN_MASK);
-              else bf = bin_chunk(cw[cb][i >> 2][i & 3], s, BIN_SIGN, BIN_TWO);
-              const u32x4 af = *(const u32x4*)(xs + i * 4096 + c16 * 256 + ((stream_chunk<TERN>(q, s) ^ c16) << 4));
-              tmp[u] = mfma16<BF16>(af, bf, s == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : tmp[u]);
-            }
-          }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (4 * bk + u < GW) acc[cb] += sc[u] * tmp[u];
       }
+      const uint8_t* xs = xw + bsel * GW * 4096;
+      float sc[GW];
+#pragma unroll
+      for (int u = 0; u < GW; ++u) {
+        const int sbits = __shfl((int)sr[bsel], 16 * u + c16);
+        sc[u] = c * GW + u < ng ? factor * half_bits_to_float((uint16_t)sbits) : 0.0f;
+      }
+      f32x4 tmp[GW];
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int u = 0; u < GW; ++u) {
+          u32x4 bf;
+          if (TERN) bf = tern_chunk(w[u >> 1][(u & 1) + 2 * (s >> 1)], s & 1, TERN_MASK);
+          else bf = bin_chunk(w[0][u], s, BIN_SIGN, BIN_TWO);
+          const u32x4 af = *(const u32x4*)(xs + u * 4096 + c16 * 256 + ((stream_chunk<TERN>(q, s) ^ c16) << 4));
+          tmp[u] = mfma16<BF16>(af, bf, s == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : tmp[u]);
+        }
+#pragma unroll
+      for (int u = 0; u < GW; ++u) acc += sc[u] * tmp[u];
     }
-    red[wave][cb][lane] = acc[cb];
+    // chunk c+2 into the buffers of chunk c (this wave's reads of them are
+    // done: their data fed the MFMAs above)
+    if (c + 2 < NCH) issue(c + 2);
   }
+  red[wave][lane] = acc;
   __syncthreads();
 
-  // (5) sum of the waves' partials in wave order, epilogue; lane holds rows
+  // sum of the waves' partials in wave order, epilogue; lane holds rows
   // 4q + e (e = 0..3) of column n
-  for (int cb = wave; cb < CB; cb += nwav) {
-    f32x4 sum = red[0][cb][lane];
-    for (int w = 1; w < nwav; ++w) sum += red[w][cb][lane];
-    const int n = col0 + 16 * cb + c16;
+  if (wave == 0) {
+    f32x4 sum = red[0][lane];
+    for (int w2 = 1; w2 < nwav; ++w2) sum += red[w2][lane];
     if (n < a.N) {
       const float b = a.bias ? load_bias(a.bias, a.bias_dtype, n) : 0.0f;
 #pragma unroll
@@ -698,22 +705,31 @@ __global__ void gelu_kernel(const void* in, void* out, int dtype, int64_t count)
 // Host-side launch helpers
 // ===========================================================================
 
-// Plan of the small-M kernel with the K split inside the workgroup: one
-// 16-column block per workgroup (CB = 1), GW groups per wave. It is used
-// only while N / 16 is below the CU count: every workgroup reads all of X
-// from L2, and for wider N the kernel above (X shared through LDS by 64 or
-// 128 columns) is faster. GW is 2, or 4 when 2 would need more than 16
-// waves; the activations of the whole K range sit in LDS, so K <= 4608.
-struct ThinPlan { int gw, cb, waves, blocks; };
+// Plan of the small-M kernel with the K split inside the workgroup: used
+// only while N / 16 is below the CU count (every workgroup reads all of X
+// from L2; for wider N the kernel above, with X shared through LDS by 64 or
+// 128 columns, is faster). One chunk per wave (all of the wave's
+// activations in LDS at once) while K allows: GW = 2 with up to 16 waves,
+// else GW = 4 within the LDS (K <= 4608). Longer K: 8 waves, chunks of
+// GW = 2 groups, 3 <= NCH <= 8 chunks per wave, two chunks in flight.
+struct ThinPlan { int gw, nch, waves, blocks; };
 
 static bool thin_plan(int M, int N, int K, int num_cu, ThinPlan* out) {
   if (M > 16 || (N + 15) / 16 >= num_cu) return false;
   const int G = K / 128;
-  const int gw = (G + 1) / 2 <= thin::MAXWAVES ? 2 : 4;
-  const int waves = (G + gw - 1) / gw;
-  if (waves > thin::MAXWAVES || (size_t)waves * gw * 4096 + 16 * 1024 > 160 * 1024)
-    return false;                                       // activations + partials in LDS
-  *out = ThinPlan{gw, 1, waves, (N + 15) / 16};
+  const int blocks = (N + 15) / 16;
+  constexpr size_t LDS = 160 * 1024, RED = 16 * 1024;      // LDS per workgroup, partials
+  if ((G + 1) / 2 <= thin::MAXWAVES) {
+    *out = ThinPlan{2, 1, (G + 1) / 2, blocks};
+    return true;
+  }
+  if ((G + 3) / 4 <= thin::MAXWAVES && (size_t)((G + 3) / 4) * 4 * 4096 + RED <= LDS) {
+    *out = ThinPlan{4, 1, (G + 3) / 4, blocks};
+    return true;
+  }
+  const int nch = (G + 2 * thin::MAXWAVES_CHUNKED - 1) / (2 * thin::MAXWAVES_CHUNKED);
+  if (nch > 8) return false;
+  *out = ThinPlan{2, nch, (G + 2 * nch - 1) / (2 * nch), blocks};
   return true;
 }
 
@@ -780,9 +796,22 @@ size_t small_workspace_bytes(int M, int N, int K, int num_cu, int variant) {
 template <bool BF16, int FMT>
 static void launch_thin_t(const GemmArgs& a, const ThinPlan& p, hipStream_t st) {
   const dim3 grid(p.blocks), block(64 * p.waves);
-  const size_t lds = (size_t)p.waves * p.gw * 4096;
-  if (p.gw == 2) hipLaunchKernelGGL((gemm_thin_kernel<BF16, FMT, 2, 1>), grid, block, lds, st, a);
-  else hipLaunchKernelGGL((gemm_thin_kernel<BF16, FMT, 4, 1>), grid, block, lds, st, a);
+  const size_t lds = (size_t)p.waves * (p.nch == 1 ? 1 : 2) * p.gw * 4096;
+#define LOWBIT_THIN(GW, NCH) hipLaunchKernelGGL((gemm_thin_kernel<BF16, FMT, GW, NCH>), grid, block, lds, st, a)
+  if (p.nch == 1) {
+    if (p.gw == 2) LOWBIT_THIN(2, 1);
+    else LOWBIT_THIN(4, 1);
+  } else {
+    switch (p.nch) {
+      case 3: LOWBIT_THIN(2, 3); break;
+      case 4: LOWBIT_THIN(2, 4); break;
+      case 5: LOWBIT_THIN(2, 5); break;
+      case 6: LOWBIT_THIN(2, 6); break;
+      case 7: LOWBIT_THIN(2, 7); break;
+      default: LOWBIT_THIN(2, 8); break;
+    }
+  }
+#undef LOWBIT_THIN
 }
 
 template <bool BF16, int FMT>

@@ -169,14 +169,16 @@ def test_special_scales_and_codes(lb):
 # ---------------------------------------------------- variants / safety ---
 
 # shapes that reach every compiled variant of the two small-M kernels: the
-# one with the K split inside the workgroup (N / 16 below the CU count, K up
-# to 4608; 2, 4 or 8 groups per wave) and the one with column tiles of 64 or
-# 128, slices of 4 .. 32 groups split into K parts, one or many K splits;
-# odd group counts, ragged N, M < 16
+# one with the K split inside the workgroup (N / 16 below the CU count; one
+# chunk of 2 or 4 groups per wave, or 3 .. 8 double-buffered chunks of 2 for
+# long K) and the one with column tiles of 64 or 128, slices of 4 .. 32
+# groups split into K parts, one or many K splits; odd group counts, ragged
+# N, M < 16
 _SMALL_SHAPES = [(5, 64, 512), (16, 3072, 3072), (7, 520, 6144), (1, 200, 12288),
                  (16, 8192, 1024), (3, 8200, 2048), (16, 18432, 3072), (2, 8192, 8192),
                  (16, 100, 16384), (16, 100, 4096), (9, 3000, 2560), (16, 1000, 4608),
-                 (4, 4000, 128), (13, 2048, 1152)]
+                 (4, 4000, 128), (13, 2048, 1152), (16, 3072, 9216), (6, 2000, 12288),
+                 (16, 300, 4736), (16, 500, 7168), (2, 1500, 13312)]
 
 
 @pytest.mark.parametrize("fmt", ["ternary", "binary"])
@@ -215,12 +217,15 @@ def test_large_m_tile_configurations(lb, force_variant, fmt, M, N, K):
 
 @pytest.mark.parametrize("fmt", ["ternary", "binary"])
 @pytest.mark.parametrize("M,N,K", [(16, 3072, 9216), (3, 3072, 12288), (1, 200, 12288)])
-def test_split_k_small_m_is_deterministic_and_reusable(lb, fmt, M, N, K):
-    """Split-K at small M: the workgroups of a column tile combine their FP32
-    partials in split order through the workspace, and the last one resets
-    its counter. Forty calls in a row on one workspace (each into a NaN-filled
-    output) must all write every element and give identical bits; a workspace
-    smaller than required is refused."""
+def test_split_k_small_m_is_deterministic_and_reusable(lb, force_variant, fmt, M, N, K):
+    """Split-K at small M (the column-tile kernel, forced: these narrow shapes
+    otherwise take the kernel with the K split inside the workgroup): the
+    workgroups of a column tile combine their FP32 partials in split order
+    through the workspace, and the last one resets its counter. Forty calls in
+    a row on one workspace (each into a NaN-filled output) must all write every
+    element and give identical bits; a workspace smaller than required is
+    refused."""
+    force_variant("small-split")
     need = lb.workspace_bytes(fmt, M, N, K)
     assert need > 0                                   # these shapes split K
     lin = wl.make_linear("split", fmt, M, N, K, seed=560 + M, p0=0.35)
