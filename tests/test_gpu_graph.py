@@ -1,0 +1,77 @@
+"""lowbit_gemm captured in a HIP graph and replayed: every replay, with new
+activations copied into the captured input between replays (eager work and a
+synchronisation in between), must give the bits of an eager call on the same
+inputs. Covers each launch path: the small-M kernel with the K split inside
+the workgroup, the column-tile small-M kernel with a cross-workgroup K split
+(tickets and partials in the workspace, which must come back to zero after
+every replay), and the large-M kernel with wide and with pair tiles."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from gpu_util import banner, dev_bits, dev_weights
+
+pytestmark = pytest.mark.gpu
+
+CASES = [  # (variant forced or None, fmt, M, N, K)
+    (None, "ternary", 16, 3072, 3072),          # thin, one chunk per wave
+    (None, "binary", 3, 3072, 9216),            # thin, chunked
+    ("small-split", "ternary", 16, 3072, 9216),  # column tiles, split K
+    ("large-wide", "ternary", 300, 2048, 1024),
+    ("large-pair", "binary", 300, 2048, 1024),
+]
+
+
+@pytest.fixture(scope="module")
+def lb():
+    import bit_weight_gemm_int2_amd as b
+    b.lib()
+    return b
+
+
+@pytest.mark.parametrize("variant,fmt,M,N,K", CASES)
+def test_graph_replay_matches_eager(lb, variant, fmt, M, N, K):
+    banner(f"graph replay {variant} {fmt} {M}x{N}x{K}")
+    old = os.environ.get("LOWBIT_FORCE_VARIANT")
+    if variant:
+        os.environ["LOWBIT_FORCE_VARIANT"] = variant
+    try:
+        lin = wl.make_linear("graph", fmt, M, N, K, seed=900 + M, p0=0.35, with_bias=True)
+        packed, s = dev_weights(fmt, lin.codes, lin.scales)
+        b = torch.from_numpy(lin.bias.view(np.int16)).cuda().view(torch.float16)
+        g = wl.generator(901)
+        xs = [dev_bits(wl.activations(g, M, K, "bf16"), "bf16") for _ in range(4)]
+        x = xs[0].clone()
+        need = lb.workspace_bytes(fmt, M, N, K)
+        if variant == "small-split":
+            assert need > 0
+        ws = lb.new_workspace(need)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        st = torch.cuda.Stream()
+        st.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(st):
+            lb.gemm(x, packed, s, fmt, bias=b, out=y, workspace=ws)          # warm-up on the capture stream
+        torch.cuda.current_stream().wait_stream(st)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=st):
+            lb.gemm(x, packed, s, fmt, bias=b, out=y, workspace=ws)
+        torch.cuda.synchronize()
+        for r, xn in enumerate(xs):
+            x.copy_(xn)                                                      # eager work between replays
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            ref = lb.gemm(xn, packed, s, fmt, bias=b, workspace=lb.new_workspace(need))
+            torch.cuda.synchronize()
+            assert torch.equal(y.view(torch.int16), ref.view(torch.int16)), f"replay {r}"
+        if need:
+            assert int(ws[: 64 * 1024].count_nonzero()) == 0                 # tickets back to zero
+    finally:
+        if old is None:
+            os.environ.pop("LOWBIT_FORCE_VARIANT", None)
+        else:
+            os.environ["LOWBIT_FORCE_VARIANT"] = old
