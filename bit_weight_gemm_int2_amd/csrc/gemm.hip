@@ -20,6 +20,8 @@
 // MFMA step s (0..7) uses its slots 64q + 8s .. +7: a lane reads its
 // activations as 16 contiguous bytes per step and its codes for the whole
 // group as one 16-byte (ternary) or 8-byte (binary) load.
+#include <cmath>
+
 #include "common.h"
 
 namespace lowbit {
@@ -842,20 +844,27 @@ static void launch_stream_t(const GemmArgs& a, const StreamPlan& p, hipStream_t 
 //  * pair: 96 x 256 tiles, 4 waves, two stages (66 KiB of LDS), so two
 //    independent workgroups share a CU: while one runs its epilogue (bias,
 //    GELU, stores) or its group-boundary rescale the other keeps the MFMA
-//    pipes busy.
-// The pair configuration is chosen when its tiles keep two workgroups on
-// every CU and its estimated time (rounds of tiles per CU slot times tile
-// area, with a 7 % bonus for the overlap, as measured on the 4608 x 9216 x
-// 3072 up-projection) beats the wide tiles' by more than 3 %.
+//    pipes busy; and with fewer tiles than CUs, the smaller tiles spread the
+//    work over more CUs.
+// The choice compares estimated times in units of tile area per CU:
+//   wide: rounds of tiles over the CUs x tile area (4-wave wide tiles, one
+//         wave per SIMD, at 0.69 of a full CU's rate);
+//   pair: at most one tile per CU: tile area / 0.69; else rounds of two
+//         tiles per CU x 2 x tile area x 0.93 (the overlap gain).
+// The rates were measured on MI355X (1536 x 3072 x 3072: 36 against 67 us;
+// 4608 x 9216 x 3072: 0.232 against 0.250 ms). Pair tiles are taken when
+// they are estimated more than 3 % faster.
 // variant: 5 forces wide tiles, 6 forces pair tiles.
 static bool large_pair(int M, int N, int num_cu, int variant) {
   if (variant == 5) return false;
   if (variant == 6) return true;
-  const int64_t tp = (int64_t)((M + 95) / 96) * ((N + 255) / 256);
-  if (N < 2048 || tp < 2 * num_cu) return false;
-  const int64_t tw = (int64_t)((M + 127) / 128) * ((N + 511) / 512);
-  const double wide = (double)((tw + num_cu - 1) / num_cu) * (128.0 * 512.0);
-  const double pair = (double)((tp + 2 * num_cu - 1) / (2 * num_cu)) * (2.0 * 96.0 * 256.0) * 0.93;
+  constexpr double ALONE = 0.69, OVERLAP = 0.93;
+  const double P = num_cu;
+  const bool w8 = N >= 2048;
+  const double tw = (double)((M + 127) / 128) * ((N + (w8 ? 511 : 255)) / (w8 ? 512 : 256));
+  const double tp = (double)((M + 95) / 96) * ((N + 255) / 256);
+  const double wide = std::ceil(tw / P) * (w8 ? 128.0 * 512.0 : 128.0 * 256.0 / ALONE);
+  const double pair = tp <= P ? 96.0 * 256.0 / ALONE : std::ceil(tp / (2 * P)) * 2.0 * 96.0 * 256.0 * OVERLAP;
   return pair < 0.97 * wide;
 }
 
