@@ -115,14 +115,16 @@ def bench_large(torch, lb, steps, warmup):
                 flop_launch=flop_launch, avg_launch_ms=avg_launch_ms, up_ms=up_ms, down_ms=down_ms)
 
 
-def bench_small(torch, lb, reps=10):
+def bench_small(torch, lb, reps=10, fuse_qkv=False):
     """Weight streaming at M = 16 and M = 1 over the 100 ternary linears of one
-    transformer pass (and the 1-bit equivalent). One code matrix is drawn per
-    distinct shape and copied into its own device buffer per linear, so every
-    launch streams distinct memory (about 0.75 GB ternary, 0.4 GB binary, far
-    above the 256 MB last-level cache)."""
+    transformer pass (and the 1-bit equivalent); with fuse_qkv, the same
+    weights with each stream's Q, K, V rows concatenated at load time (80
+    launches). One code matrix is drawn per distinct shape and copied into its
+    own device buffer per linear, so every launch streams distinct memory
+    (about 0.75 GB ternary, 0.4 GB binary, far above the 256 MB last-level
+    cache)."""
     import workloads as wl
-    shapes = wl.mmdit_linear_shapes()
+    shapes = wl.mmdit_linear_shapes(fuse_qkv)
     distinct = sorted({(N, K) for _, N, K in shapes})
     out = {}
     for fmt in ("ternary", "binary"):
@@ -386,6 +388,7 @@ def main():
     achieved = r["flop_launch"] / (r["avg_launch_ms"] * 1e-3) / 1e12
     traffic = load_traffic()
     small = None if args.no_small else bench_small(torch, lb)
+    small_fused = None if args.no_small else bench_small(torch, lb, fuse_qkv=True)
     cpu = None if args.no_cpu else cpu_baseline()
     out = {
         "metric": METRIC,
@@ -421,6 +424,7 @@ def main():
         },
         "cpu_baseline": cpu,
         "small_m": small,
+        "small_m_fused_qkv": small_fused,
     }
     print(json.dumps(out), flush=True)
 

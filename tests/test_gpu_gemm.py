@@ -248,6 +248,31 @@ def test_split_k_small_m_is_deterministic_and_reusable(lb, force_variant, fmt, M
         lb.gemm(x, packed, s, fmt, workspace=ws[: need // 2])
 
 
+@pytest.mark.parametrize("M", [16, 1536])
+def test_same_input_linears_fused_by_concatenated_rows(lb, M):
+    """Linears that share an input (Q, K, V) run as one launch over their
+    packed rows and scales concatenated along N (the packed layout is row-major
+    in N, so concatenating packed rows equals packing the concatenated codes);
+    each column slice of the fused output meets the bound against its own
+    linear, and the packed bytes match the separate packs exactly."""
+    g = wl.generator(950 + M)
+    K = 3072
+    x = wl.activations(g, M, K, "bf16")
+    lins = [wl.make_linear(f"qkv{i}", "ternary", M, 3072, K, g=g, x=x, p0=0.35) for i in range(3)]
+    parts = [dev_weights("ternary", l.codes, l.scales) for l in lins]
+    packed = torch.cat([p for p, _ in parts], dim=0)
+    scales = torch.cat([sc for _, sc in parts], dim=0)
+    whole, _ = dev_weights("ternary", np.concatenate([l.codes for l in lins], axis=0),
+                           np.concatenate([l.scales for l in lins], axis=0))
+    assert torch.equal(packed, whole)
+    y = lb.gemm(dev_bits(x, "bf16"), packed, scales, "ternary", out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    Y = to_host64(y)
+    for i, l in enumerate(lins):
+        A, Mg = oracle_linear(l)
+        _assert_parity(Y[:, 3072 * i: 3072 * (i + 1)], A, Mg, "f32", f"fused slice {i}")
+
+
 def test_very_long_k_small_m(lb):
     """A long K with an odd group count (129 groups: many splits, a short last one)."""
     lin = wl.make_linear("longk", "ternary", 2, 64, 129 * 128, seed=550, p0=0.35)

@@ -192,19 +192,26 @@ HIDDEN = 3072
 MLP = 3 * HIDDEN
 
 
-def mmdit_linear_shapes():
-    """List of (name, N, K) for the 100 ternary linears of one transformer pass."""
+def mmdit_linear_shapes(fuse_qkv: bool = False):
+    """List of (name, N, K) for the 100 ternary linears of one transformer pass;
+    with fuse_qkv, the Q, K and V linears of each double-stream stream (same
+    input) are one [9216x3072] linear with their packed rows concatenated,
+    80 linears in all."""
     shapes = []
     for b in range(5):
         for s in ("img", "txt"):
-            for p in ("q", "k", "v", "out"):
-                shapes.append((f"double{b}.{s}.{p}", HIDDEN, HIDDEN))
+            if fuse_qkv:
+                shapes.append((f"double{b}.{s}.qkv", 3 * HIDDEN, HIDDEN))
+                shapes.append((f"double{b}.{s}.out", HIDDEN, HIDDEN))
+            else:
+                for p in ("q", "k", "v", "out"):
+                    shapes.append((f"double{b}.{s}.{p}", HIDDEN, HIDDEN))
             shapes.append((f"double{b}.{s}.mlp_in", MLP, HIDDEN))
             shapes.append((f"double{b}.{s}.mlp_out", HIDDEN, MLP))
     for b in range(20):
         shapes.append((f"single{b}.qkv_mlp_in", 3 * HIDDEN + MLP, HIDDEN))
         shapes.append((f"single{b}.out_mlp_out", HIDDEN, HIDDEN + MLP))
-    assert len(shapes) == 100
+    assert len(shapes) == (80 if fuse_qkv else 100)
     return shapes
 
 
