@@ -248,11 +248,11 @@ def traffic_summary(fetch_csv: str, write_csv: str) -> dict:
     out["bytes_per_launch"] = int(round(total / 2))
     out["commands"] = [
         "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv "
-        "-d $REPO/gpurun_out/tr_FETCH_SIZE -o run -- python $REPO/bench.py --traffic-probe",
+        "-d $OUT/tr_FETCH_SIZE -o run -- python $REPO/bench.py --traffic-probe",
         "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv "
-        "-d $REPO/gpurun_out/tr_WRITE_SIZE -o run -- python $REPO/bench.py --traffic-probe",
-        "python bench.py --traffic-summary $REPO/gpurun_out/tr_FETCH_SIZE/run_counter_collection.csv "
-        "$REPO/gpurun_out/tr_WRITE_SIZE/run_counter_collection.csv",
+        "-d $OUT/tr_WRITE_SIZE -o run -- python $REPO/bench.py --traffic-probe",
+        "python bench.py --traffic-summary $OUT/tr_FETCH_SIZE/run_counter_collection.csv "
+        "$OUT/tr_WRITE_SIZE/run_counter_collection.csv",
     ]
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(out, f, indent=2)
