@@ -378,7 +378,7 @@ __global__ __launch_bounds__(64 * WC * stream::kparts(WC, GS)) void gemm_stream_
   // (1) activations of the slice -> LDS: instruction t of this wave covers
   // rows 4j .. 4j+3 of group i (slot i of the tile)
 #pragma unroll
-  for (int t = 0; t < 4 * GS / NT; ++t) {
+  for (int t = 0; t < (4 * GS + NT - 1) / NT; ++t) {     // (group slot, row quad) pairs over the waves
     const int idx = t * NT + wave;
     const int i = idx >> 2, j = idx & 3;
     if (i < ng) {                                       // wave-uniform
@@ -735,9 +735,9 @@ static bool thin_plan(int M, int N, int K, int num_cu, ThinPlan* out) {
   return true;
 }
 
-// Small-M plan: tiles of 64 columns (4 column waves), or 128 (8) when that
-// still gives at least 128 tiles; then the K split S (1 .. MAXSPLIT, at most
-// MAXGS groups per slice) that minimises a rough time estimate:
+// Small-M plan: the tile width (16 WC columns, WC in 3, 4, 5, 6, 8) and the
+// K split S (1 .. MAXSPLIT, at most MAXGS groups per slice) that minimise a
+// rough time estimate:
 //   rounds * (slice bytes through one CU at ~64 B/clk + slice MFMA work
 //   shared by the slice's K parts)
 //   + a fixed cost for the cross-workgroup combine when S > 1
@@ -751,12 +751,12 @@ static int round_gs(int g) { return g <= 4 ? 4 : g <= 8 ? 8 : g <= 12 ? 12 : g <
 static bool stream_plan(int M, int N, int K, int num_cu, StreamPlan* out) {
   if (M > 16) return false;
   const int G = K / 128;
-  const int t8 = (N + 127) / 128, t4 = (N + 63) / 64;
-  const int wc = t8 >= 128 ? 8 : 4;
-  const int tiles = wc == 8 ? t8 : t4;
-  if (tiles > stream::MAXTILES || G > stream::MAXGS * stream::MAXSPLIT) return false;
+  if (G > stream::MAXGS * stream::MAXSPLIT) return false;
   double best = 1e30;
   StreamPlan bp{};
+  for (int wc : {3, 4, 5, 6, 8}) {
+  const int tiles = (N + 16 * wc - 1) / (16 * wc);
+  if (tiles > stream::MAXTILES) continue;
   for (int sp = 1; sp <= min(stream::MAXSPLIT, G); ++sp) {
     const int gps = (G + sp - 1) / sp;
     if (gps > stream::MAXGS) continue;
@@ -772,6 +772,7 @@ static bool stream_plan(int M, int N, int K, int num_cu, StreamPlan* out) {
       best = us;
       bp = StreamPlan{wc, gs, gps, S, tiles};
     }
+  }
   }
   *out = bp;
   return best < 1e29;
@@ -829,10 +830,12 @@ static void launch_stream_t(const GemmArgs& a, const StreamPlan& p, hipStream_t 
   else if (p.gs == 16) LOWBIT_STREAM(WC, 16); \
   else if (p.gs == 24) LOWBIT_STREAM(WC, 24); \
   else LOWBIT_STREAM(WC, 32);
-  if (p.wc == 8) {
-    LOWBIT_STREAM_GS(8)
-  } else {
-    LOWBIT_STREAM_GS(4)
+  switch (p.wc) {
+    case 3: LOWBIT_STREAM_GS(3) break;
+    case 4: LOWBIT_STREAM_GS(4) break;
+    case 5: LOWBIT_STREAM_GS(5) break;
+    case 6: LOWBIT_STREAM_GS(6) break;
+    default: LOWBIT_STREAM_GS(8) break;
   }
 #undef LOWBIT_STREAM_GS
 #undef LOWBIT_STREAM

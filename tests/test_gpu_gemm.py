@@ -171,14 +171,15 @@ def test_special_scales_and_codes(lb):
 # shapes that reach every compiled variant of the two small-M kernels: the
 # one with the K split inside the workgroup (N / 16 below the CU count; one
 # chunk of 2 or 4 groups per wave, or 3 .. 8 double-buffered chunks of 2 for
-# long K) and the one with column tiles of 64 or 128, slices of 4 .. 32
-# groups split into K parts, one or many K splits; odd group counts, ragged
-# N, M < 16
+# long K) and the one with column tiles of 48 .. 128 columns (3, 4, 5, 6, 8
+# column waves), slices of 4 .. 32 groups split into K parts, one or many K
+# splits; odd group counts, ragged N, M < 16
 _SMALL_SHAPES = [(5, 64, 512), (16, 3072, 3072), (7, 520, 6144), (1, 200, 12288),
                  (16, 8192, 1024), (3, 8200, 2048), (16, 18432, 3072), (2, 8192, 8192),
                  (16, 100, 16384), (16, 100, 4096), (9, 3000, 2560), (16, 1000, 4608),
                  (4, 4000, 128), (13, 2048, 1152), (16, 3072, 9216), (6, 2000, 12288),
-                 (16, 300, 4736), (16, 500, 7168), (2, 1500, 13312)]
+                 (16, 300, 4736), (16, 500, 7168), (2, 1500, 13312), (16, 22000, 3072),
+                 (5, 30000, 3072)]
 
 
 @pytest.mark.parametrize("fmt", ["ternary", "binary"])
