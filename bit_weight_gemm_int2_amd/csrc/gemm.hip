@@ -311,7 +311,14 @@ __global__ __launch_bounds__(64 * WN) void gemm_large_kernel(GemmArgs a, int til
 //    column) or one group (binary: 16 bytes = 128 codes), so a wave-wide
 //    instruction reads 64 contiguous bytes per column. v_permlane32_swap
 //    (and v_permlane16_swap for binary) then hands every lane its own share
-//    of each group. All loads of the slice are issued before one wait.
+//    of each group.
+//  * Load order: all activation DMAs first (from inline assembly, so the
+//    compiler neither counts them nor makes LDS reads wait for them), then
+//    the codes and scales block by block (a block is four groups of a K
+//    part). One explicit wait and a barrier cover the activations; each
+//    block's MFMAs then wait only for that block's codes, so the later
+//    blocks' code loads are still in flight while the earlier blocks are
+//    computed.
 //  * MFMA rows are output rows, MFMA columns are output columns; each group
 //    is four chained MFMAs, then acc += (scale * factor) * tmp in FP32. Four
 //    groups are interleaved (four independent chains); slots past the slice
@@ -376,15 +383,20 @@ __global__ __launch_bounds__(64 * WC * stream::kparts(WC, GS)) void gemm_stream_
   const float factor = code_factor<TERN>();
 
   // (1) activations of the slice -> LDS: instruction t of this wave covers
-  // rows 4j .. 4j+3 of group i (slot i of the tile)
+  // rows 4j .. 4j+3 of group i (slot i of the tile). Issued from inline
+  // assembly (scalar base + lane offset), so the compiler neither counts them
+  // in its own waits nor makes LDS reads wait for them: one explicit wait
+  // below covers them all.
+  constexpr int NB = GH / 4;                           // blocks of four groups per K part
+  constexpr int CB = TERN ? 2 : 1;                     // code loads per block
 #pragma unroll
   for (int t = 0; t < (4 * GS + NT - 1) / NT; ++t) {     // (group slot, row quad) pairs over the waves
     const int idx = t * NT + wave;
     const int i = idx >> 2, j = idx & 3;
     if (i < ng) {                                       // wave-uniform
       const int r = 4 * j + q;                          // tile row of this lane
-      const uint16_t* src = a.X + (int64_t)min(r, a.M - 1) * a.ldx + ((g0 + i) << 7) + 8 * ((c16 ^ r) & 15);
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr_t)(smem + i * 4096 + j * 1024), 16, 0, 0);
+      const uint32_t voff = (uint32_t)(((int64_t)min(r, a.M - 1) * a.ldx + 8 * ((c16 ^ r) & 15)) * 2);
+      dma_lds16((const uint8_t*)a.X + ((int64_t)(g0 + i) << 8), voff, lds_addr(smem + i * 4096 + j * 1024));
     }
   }
   // slots past the slice up to the next multiple of 4 are computed with zero
@@ -394,51 +406,59 @@ __global__ __launch_bounds__(64 * WC * stream::kparts(WC, GS)) void gemm_stream_
     for (int z = ng * 256 + tid; z < zend * 256; z += 64 * NT)
       *(u32x4*)(smem + (size_t)z * 16) = u32x4{0u, 0u, 0u, 0u};
   }
-  // (2) codes of this wave's K part (slots gk0 + 2p, gk0 + 2p + 1, ...):
-  // ternary load p covers slots 2p (lane groups 0, 1) and 2p+1 (lane groups
-  // 2, 3); binary load p: lane group q reads slot 4p + q
+  // (2) codes and raw scales of this wave's K part, block by block (a block
+  // is four groups), so each block's MFMAs wait only for its own codes and
+  // the later blocks' loads stay in flight meanwhile. Ternary load p covers
+  // slots gk0 + 2p (lane groups 0, 1) and gk0 + 2p + 1 (lane groups 2, 3);
+  // binary load p: lane group q reads slot gk0 + 4p + q; scale word b: lane
+  // group q holds slot gk0 + 4b + q of its column
   const uint8_t* wp = a.W + nc * wrow;
   u32x4 cw[NW];
+  uint32_t sr[NB];
 #pragma unroll
-  for (int p = 0; p < NW; ++p) {
-    if (TERN) {
-      const int g = g0 + min(gk0 + 2 * p + (q >> 1), ng - 1);
-      cw[p] = *(const u32x4*)(wp + g * 32 + 16 * (q & 1));
-    } else {
-      const int g = g0 + min(gk0 + 4 * p + q, ng - 1);
-      cw[p] = *(const u32x4*)(wp + g * 16);
+  for (int b = 0; b < NB; ++b) {
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {
+      const int p = CB * b + c;
+      if (TERN) {
+        const int g = g0 + min(gk0 + 2 * p + (q >> 1), ng - 1);
+        cw[p] = *(const u32x4*)(wp + g * 32 + 16 * (q & 1));
+      } else {
+        const int g = g0 + min(gk0 + 4 * p + q, ng - 1);
+        cw[p] = *(const u32x4*)(wp + g * 16);
+      }
     }
+    sr[b] = a.S[nc * G + g0 + min(gk0 + 4 * b + q, ng - 1)];
   }
-  // (3) raw scales: lane group q holds slots gk0 + 4j + q of its column
-  uint32_t sr[GH / 4];
-#pragma unroll
-  for (int j = 0; j < GH / 4; ++j) sr[j] = a.S[nc * G + g0 + min(gk0 + 4 * j + q, ng - 1)];
-  __builtin_amdgcn_s_waitcnt(0);                        // this wave's loads and LDS DMA
-  __syncthreads();                                      // everyone's LDS DMA
+  // every activation DMA of this wave done (only the NB (CB + 1) register
+  // loads above, issued after them, may be in flight), then everyone's
+  __builtin_amdgcn_s_waitcnt(large::waitcnt_vm(NB * (CB + 1)));
+  __syncthreads();
 
-  // (4) lane exchange: afterwards ternary group 2p is in (cw[p][0], cw[p][2])
-  // and group 2p+1 in (cw[p][1], cw[p][3]); binary group 4p+j is cw[p][j]
-#pragma unroll
-  for (int p = 0; p < NW; ++p) {
-    if (TERN) {
-      auto x = __builtin_amdgcn_permlane32_swap(cw[p][0], cw[p][1], false, false);
-      auto y = __builtin_amdgcn_permlane32_swap(cw[p][2], cw[p][3], false, false);
-      cw[p] = u32x4{x[0], x[1], y[0], y[1]};
-    } else {
-      auto x = __builtin_amdgcn_permlane32_swap(cw[p][0], cw[p][2], false, false);
-      auto y = __builtin_amdgcn_permlane32_swap(cw[p][1], cw[p][3], false, false);
-      auto u = __builtin_amdgcn_permlane16_swap(x[0], y[0], false, false);
-      auto v = __builtin_amdgcn_permlane16_swap(x[1], y[1], false, false);
-      cw[p] = u32x4{u[0], u[1], v[0], v[1]};
-    }
-  }
-
-  // (5) MFMAs, four groups at a time: four independent chains, no branch
-  // inside a block (groups past the slice read zero activations)
+  // (3) per block: lane exchange (afterwards ternary group 2p is in
+  // (cw[p][0], cw[p][2]) and group 2p+1 in (cw[p][1], cw[p][3]); binary
+  // group 4p+j is cw[p][j]), then the MFMAs, four groups at a time: four
+  // independent chains, no branch inside a block (groups past the slice
+  // read zero activations)
   f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int bk = 0; bk < GH / 4; ++bk) {
+  for (int bk = 0; bk < NB; ++bk) {
     if (gk0 + 4 * bk < ng) {                            // wave-uniform
+#pragma unroll
+      for (int c = 0; c < CB; ++c) {
+        const int p = CB * bk + c;
+        if (TERN) {
+          auto x = __builtin_amdgcn_permlane32_swap(cw[p][0], cw[p][1], false, false);
+          auto y = __builtin_amdgcn_permlane32_swap(cw[p][2], cw[p][3], false, false);
+          cw[p] = u32x4{x[0], x[1], y[0], y[1]};
+        } else {
+          auto x = __builtin_amdgcn_permlane32_swap(cw[p][0], cw[p][2], false, false);
+          auto y = __builtin_amdgcn_permlane32_swap(cw[p][1], cw[p][3], false, false);
+          auto u = __builtin_amdgcn_permlane16_swap(x[0], y[0], false, false);
+          auto v = __builtin_amdgcn_permlane16_swap(x[1], y[1], false, false);
+          cw[p] = u32x4{u[0], u[1], v[0], v[1]};
+        }
+      }
       float sc[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
