@@ -301,11 +301,14 @@ __global__ __launch_bounds__(64 * WN) void gemm_large_kernel(GemmArgs a, int til
 // output columns and one slice of at most GS 128-groups of K; its WC x KH
 // waves are WC column waves (16 columns each) times KH parts of the slice
 // along K, whose FP32 results meet in LDS and are added in part order:
-//  * The activations of the slice (rows >= M repeat row M - 1: MFMA rows are
-//    independent and those outputs are never stored) go global -> LDS once
-//    per workgroup with direct LDS DMA loads, each instruction reading four
-//    whole 256-byte group rows; 16-byte chunks are XOR-swizzled by row, which
-//    makes the MFMA fragment reads conflict-free.
+//  * The activations of the slice go global -> LDS once per workgroup with
+//    direct LDS DMA loads, each instruction reading four whole 256-byte group
+//    rows; 16-byte chunks are XOR-swizzled by row, which makes the MFMA
+//    fragment reads conflict-free. Only the ceil(M / 4) row quads that hold
+//    rows < M are copied (rounded to 1, 2 or 4; rows past M inside a quad
+//    repeat row M - 1), and the fragment reads of the rows past them use row
+//    r & (4 quads - 1): MFMA rows are independent and outputs of rows >= M
+//    are never stored.
 //  * Codes: every lane issues 16-byte loads that cover two groups of its
 //    column (ternary: the four lane groups read 64 contiguous bytes of the
 //    column) or one group (binary: 16 bytes = 128 codes), so a wave-wide
@@ -389,10 +392,15 @@ __global__ __launch_bounds__(64 * WC * stream::kparts(WC, GS)) void gemm_stream_
   // below covers them all.
   constexpr int NB = GH / 4;                           // blocks of four groups per K part
   constexpr int CB = TERN ? 2 : 1;                     // code loads per block
+  // only the row quads that hold rows < M are copied (rq of 1, 2 or 4);
+  // fragment reads of rows past them read row r & (4 rq - 1) instead:
+  // MFMA rows are independent and outputs of rows >= M are never stored
+  const int lrq = a.M <= 4 ? 0 : a.M <= 8 ? 1 : 2, rq = 1 << lrq;
+  const int rr = c16 & (4 * rq - 1);                   // LDS row of this lane's fragment reads
 #pragma unroll
   for (int t = 0; t < (4 * GS + NT - 1) / NT; ++t) {     // (group slot, row quad) pairs over the waves
     const int idx = t * NT + wave;
-    const int i = idx >> 2, j = idx & 3;
+    const int i = idx >> lrq, j = idx & (rq - 1);
     if (i < ng) {                                       // wave-uniform
       const int r = 4 * j + q;                          // tile row of this lane
       const uint32_t voff = (uint32_t)(((int64_t)min(r, a.M - 1) * a.ldx + 8 * ((c16 ^ r) & 15)) * 2);
@@ -471,7 +479,7 @@ __global__ __launch_bounds__(64 * WC * stream::kparts(WC, GS)) void gemm_stream_
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int i = 4 * bk + u;                     // slot within the K part
-          const u32x4 af = *(const u32x4*)(smem + (gk0 + i) * 4096 + c16 * 256 + ((stream_chunk<TERN>(q, s) ^ c16) << 4));
+          const u32x4 af = *(const u32x4*)(smem + (gk0 + i) * 4096 + rr * 256 + ((stream_chunk<TERN>(q, s) ^ rr) << 4));
           u32x4 bf;
           if (TERN) bf = tern_chunk(cw[i >> 1][(i & 1) + 2 * (s >> 1)], s & 1, TERN_MASK);
           else bf = bin_chunk(cw[i >> 2][i & 3], s, BIN_SIGN, BIN_TWO);
@@ -559,8 +567,8 @@ __global__ __launch_bounds__(64 * WC * stream::kparts(WC, GS)) void gemm_stream_
 // GW groups. Per wave and chunk:
 //  * the activations of the chunk's groups go to the wave's own LDS region
 //    by direct LDS DMA (whole 256-byte group rows, chunks XOR-swizzled by
-//    row as in the kernel above; rows >= M repeat row M - 1, whose outputs
-//    are never stored), so only the wave's own wait is needed before it
+//    row as in the kernel above; only the row quads that hold rows < M, as
+//    in the kernel above), so only the wave's own wait is needed before it
 //    reads them; the codes come as 16-byte loads covering two groups
 //    (ternary) or one group (binary) per lane, exchanged with
 //    v_permlane32_swap / v_permlane16_swap exactly as in the kernel above;
@@ -609,6 +617,11 @@ __global__ __launch_bounds__(64 * (NCH == 1 ? thin::MAXWAVES : thin::MAXWAVES_CH
   const int64_t nc = min(n, a.N - 1);                       // columns past N: any valid column
   const uint8_t* wp = a.W + nc * wrow;
   uint8_t* xw = smem + (size_t)wave * NBUF * GW * 4096;
+  // only the row quads that hold rows < M are copied (rq of 1, 2 or 4);
+  // fragment reads of rows past them read row r & (4 rq - 1) instead:
+  // MFMA rows are independent and outputs of rows >= M are never stored
+  const int rq = a.M <= 4 ? 1 : a.M <= 8 ? 2 : 4;
+  const int rr = c16 & (4 * rq - 1);                        // LDS row of this lane's fragment reads
 
   u32x4 cw[NBUF][NW];
   uint32_t sr[NBUF];
@@ -621,6 +634,7 @@ __global__ __launch_bounds__(64 * (NCH == 1 ? thin::MAXWAVES : thin::MAXWAVES_CH
       const int gi = g0 + min(c * GW + i, ng - 1);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
+        if (j >= rq) continue;                              // wave-uniform: rows >= 4 rq not needed
         const int r = 4 * j + q;                            // row of this lane
         const uint16_t* src = a.X + (int64_t)min(r, a.M - 1) * a.ldx + (gi << 7) + 8 * ((c16 ^ r) & 15);
         __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr_t)(xs + i * 4096 + j * 1024), 16, 0, 0);
@@ -647,8 +661,13 @@ __global__ __launch_bounds__(64 * (NCH == 1 ? thin::MAXWAVES : thin::MAXWAVES_CH
   for (int c = 0; c < NCH; ++c) {
     const int bsel = c % NBUF;
     // chunk c has landed (the loads of chunk c+1 may still be in flight)
-    if (c + 1 < NCH) __builtin_amdgcn_s_waitcnt(large::waitcnt_vm(XDMA));
-    else __builtin_amdgcn_s_waitcnt(0);
+    if (c + 1 < NCH) {
+      if (rq == 1) __builtin_amdgcn_s_waitcnt(large::waitcnt_vm(XDMA / 4));
+      else if (rq == 2) __builtin_amdgcn_s_waitcnt(large::waitcnt_vm(XDMA / 2));
+      else __builtin_amdgcn_s_waitcnt(large::waitcnt_vm(XDMA));
+    } else {
+      __builtin_amdgcn_s_waitcnt(0);
+    }
     if (c * GW < ng) {                                      // wave-uniform
       // lane exchange (as in the kernel above)
       u32x4 w[NW];
@@ -681,7 +700,7 @@ __global__ __launch_bounds__(64 * (NCH == 1 ? thin::MAXWAVES : thin::MAXWAVES_CH
           u32x4 bf;
           if (TERN) bf = tern_chunk(w[u >> 1][(u & 1) + 2 * (s >> 1)], s & 1, TERN_MASK);
           else bf = bin_chunk(w[0][u], s, BIN_SIGN, BIN_TWO);
-          const u32x4 af = *(const u32x4*)(xs + u * 4096 + c16 * 256 + ((stream_chunk<TERN>(q, s) ^ c16) << 4));
+          const u32x4 af = *(const u32x4*)(xs + u * 4096 + rr * 256 + ((stream_chunk<TERN>(q, s) ^ rr) << 4));
           tmp[u] = mfma16<BF16>(af, bf, s == 0 ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : tmp[u]);
         }
 #pragma unroll

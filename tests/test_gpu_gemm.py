@@ -179,7 +179,7 @@ _SMALL_SHAPES = [(5, 64, 512), (16, 3072, 3072), (7, 520, 6144), (1, 200, 12288)
                  (16, 100, 16384), (16, 100, 4096), (9, 3000, 2560), (16, 1000, 4608),
                  (4, 4000, 128), (13, 2048, 1152), (16, 3072, 9216), (6, 2000, 12288),
                  (16, 300, 4736), (16, 500, 7168), (2, 1500, 13312), (16, 22000, 3072),
-                 (5, 30000, 3072)]
+                 (5, 30000, 3072), (4, 3072, 9216), (8, 9216, 3072), (12, 520, 6144), (4, 3072, 3072)]
 
 
 @pytest.mark.parametrize("fmt", ["ternary", "binary"])
