@@ -5,6 +5,7 @@
 
 #include <atomic>
 #include <cstdlib>
+#include <algorithm>
 #include <cstring>
 #include <mutex>
 
@@ -70,6 +71,9 @@ int force_variant() {
 }
 
 constexpr int64_t kMaxDim = (int64_t)1 << 31;
+// largest operand byte span the kernels' 32-bit offsets cover (with room
+// for the last 16-byte load)
+constexpr int64_t kOffsetSpan = ((int64_t)1 << 32) - 64;
 
 }  // namespace
 
@@ -168,7 +172,17 @@ int32_t lowbit_gemm(int32_t format, const void* X, int32_t x_dtype, int64_t M, i
   if ((bias == nullptr) != (bias_dtype == LOWBIT_NONE)) return bias ? LOWBIT_ERR_DTYPE : LOWBIT_ERR_NULL;
   if (M < 1 || N < 1 || K < 128 || K % 128 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim)
     return LOWBIT_ERR_SHAPE;
-  if (ldx < K || ldy < N) return LOWBIT_ERR_SHAPE;
+  if (ldx < K || ldy < N || ldx >= kMaxDim || ldy >= kMaxDim) return LOWBIT_ERR_SHAPE;
+  // The kernels address the packed codes (and scales) of a column, and the
+  // activations of a row, by 32-bit byte offsets from the operand's base:
+  // the packed weights must span less than 4 GiB; X is taken in row chunks
+  // whose offsets fit (below).
+  const int64_t wrow = format == LOWBIT_TERNARY_INT2 ? K / 4 : K / 8;
+  if (N * wrow > kOffsetSpan) return LOWBIT_ERR_SHAPE;
+  const int64_t rows_max = (kOffsetSpan - 2 * K) / (2 * ldx) + 1;   // rows whose X offsets fit
+  // a problem with M > 16 keeps every chunk above 16 rows (same kernels and
+  // workspace as the whole problem)
+  if (M > 16 && M > rows_max && rows_max < 34) return LOWBIT_ERR_SHAPE;
   const size_t ysz = y_dtype == LOWBIT_F32 ? 4 : 2;
   if (!aligned(X, 16) || !aligned(W_packed, 16) || !aligned(scales, 2) || !aligned(Y, ysz) || ldx % 8)
     return LOWBIT_ERR_ALIGN;
@@ -181,24 +195,31 @@ int32_t lowbit_gemm(int32_t format, const void* X, int32_t x_dtype, int64_t M, i
   if (need && !aligned(workspace, 256)) return LOWBIT_ERR_ALIGN;
 
   lowbit::GemmArgs a{};
-  a.X = (const uint16_t*)X;
   a.ldx = ldx;
   a.W = W_packed;
   a.S = (const uint16_t*)scales;
   a.bias = bias;
   a.bias_dtype = bias_dtype;
-  a.Y = Y;
   a.ldy = ldy;
   a.y_dtype = y_dtype;
   a.act = activation;
-  a.M = (int)M;
   a.N = (int)N;
   a.K = (int)K;
   a.ws = (float*)workspace;
   const int variant = force_variant();
-  hipError_t e = lowbit::launch_gemm(format == LOWBIT_TERNARY_INT2 ? lowbit::FMT_TERNARY : lowbit::FMT_BINARY,
-                                     x_dtype == LOWBIT_BF16, a, num_cu, variant, (hipStream_t)stream);
-  return e == hipSuccess ? LOWBIT_OK : LOWBIT_ERR_HIP;
+  // one launch unless X spans 4 GiB or more; then equal row chunks, in order
+  // on the stream (they may share the workspace)
+  const int64_t nchunks = M <= rows_max ? 1 : (M + rows_max - 1) / rows_max;
+  const int64_t chunk = (M + nchunks - 1) / nchunks;
+  for (int64_t m0 = 0; m0 < M; m0 += chunk) {
+    a.X = (const uint16_t*)X + m0 * ldx;
+    a.Y = (uint8_t*)Y + m0 * ldy * (int64_t)ysz;
+    a.M = (int)std::min(chunk, M - m0);
+    hipError_t e = lowbit::launch_gemm(format == LOWBIT_TERNARY_INT2 ? lowbit::FMT_TERNARY : lowbit::FMT_BINARY,
+                                       x_dtype == LOWBIT_BF16, a, num_cu, variant, (hipStream_t)stream);
+    if (e != hipSuccess) return LOWBIT_ERR_HIP;
+  }
+  return LOWBIT_OK;
 }
 
 int32_t lowbit_gelu(const void* in, void* out, int32_t dtype, int64_t count, void* stream) {

@@ -131,13 +131,19 @@ size_t lowbit_gemm_workspace_bytes(int32_t format, int64_t M, int64_t N, int64_t
  *
  *   format      LOWBIT_TERNARY_INT2 or LOWBIT_BINARY_1BIT
  *   X           [M][ldx] of x_dtype (LOWBIT_F16 or LOWBIT_BF16); 16-byte
- *               aligned, ldx >= K, ldx % 8 == 0
- *   W_packed    [N][K/4] or [N][K/8] bytes in the packed layout, 16-byte aligned
+ *               aligned, K <= ldx < 2^31, ldx % 8 == 0. When X spans 4 GiB
+ *               or more ((M-1)*ldx*2 + 2K bytes) it is processed in equal row
+ *               chunks that span less, one launch each, in order on the
+ *               stream; for M > 16 the chunks must stay above 16 rows
+ *               (ldx below about 2^27), else LOWBIT_ERR_SHAPE
+ *   W_packed    [N][K/4] or [N][K/8] bytes in the packed layout, 16-byte
+ *               aligned, spanning less than 4 GiB (N*K/4 or N*K/8 bytes),
+ *               else LOWBIT_ERR_SHAPE
  *   scales      FP16 [N][K/group], 2-byte aligned; group must be 128
  *   bias        nullable; [N] of bias_dtype (F16, BF16, F32), or
  *               bias_dtype = LOWBIT_NONE with bias = NULL
  *   Y           [M][ldy] of y_dtype (F16, BF16, F32); aligned to its element
- *               size, ldy >= N; must not overlap X, W, scales, bias
+ *               size, N <= ldy < 2^31; must not overlap X, W, scales, bias
  *   activation  LOWBIT_ACT_NONE or LOWBIT_ACT_GELU_ERF (x * Phi(x), exact erf)
  *   workspace   device scratch of at least lowbit_gemm_workspace_bytes(),
  *               256-byte aligned; may be NULL when that is 0. Its bytes must

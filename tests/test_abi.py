@@ -89,6 +89,13 @@ def test_argument_errors_before_any_device_work(L):
     assert call(N=0) == b.ERR_SHAPE
     assert call(ldx=128) == b.ERR_SHAPE                       # ldx < K
     assert call(ldy=32) == b.ERR_SHAPE
+    assert call(ldx=1 << 31) == b.ERR_SHAPE                  # ldx >= 2^31
+    assert call(ldy=1 << 31) == b.ERR_SHAPE
+    # packed weights spanning 4 GiB (32-bit column offsets): N * K / 4 bytes
+    assert call(N=1 << 20, ldy=1 << 20, K=1 << 14, ldx=1 << 14) == b.ERR_SHAPE
+    assert call(fmt=b.BINARY, N=1 << 20, ldy=1 << 20, K=1 << 15, ldx=1 << 15) == b.ERR_SHAPE
+    # M > 16 whose X row chunks under 4 GiB would be 16 rows or fewer
+    assert call(M=64, ldx=(1 << 27) + 8) == b.ERR_SHAPE
     assert call(X=P + 8) == b.ERR_ALIGN
     assert call(ldx=260) == b.ERR_ALIGN
     assert call(Y=P + 2, yd=b.F32) == b.ERR_ALIGN

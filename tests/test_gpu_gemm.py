@@ -216,6 +216,26 @@ def test_large_m_tile_configurations(lb, force_variant, fmt, M, N, K):
     assert not (np.abs(Yg - G) > lim).any()
 
 
+@pytest.mark.parametrize("M,N,K,ldx", [(4200, 512, 256, 1 << 19),         # large-M kernel, 2 chunks
+                                         (16, 8192, 256, 150_000_000),     # column tiles, 2 chunks of 8
+                                         (5, 640, 256, 600_000_000)])      # thin kernel, chunks of 3 and 2
+def test_activations_spanning_4gib_run_in_row_chunks(lb, M, N, K, ldx):
+    """X whose row stride makes it span 4 GiB or more: the kernels address X
+    by 32-bit byte offsets, so the library runs it in row chunks that span
+    less. Every row must meet the bound (4.4 to 5 GB of device memory)."""
+    banner(f"strided X {M}x{N}x{K} ldx={ldx}")
+    lin = wl.make_linear("stride", "ternary", M, N, K, seed=610 + M, p0=0.35, with_bias=False)
+    A, Mg = oracle_linear(lin)
+    xs = torch.empty((M, ldx), dtype=torch.bfloat16, device="cuda")
+    xs[:, :K] = dev_bits(lin.x, "bf16")
+    packed, s = dev_weights("ternary", lin.codes, lin.scales)
+    y = lb.gemm(xs[:, :K], packed, s, "ternary")
+    torch.cuda.synchronize()
+    del xs
+    torch.cuda.empty_cache()
+    _assert_parity(to_host64(y), A, Mg, "bf16", f"strided X ldx={ldx}")
+
+
 @pytest.mark.parametrize("fmt", ["ternary", "binary"])
 @pytest.mark.parametrize("M,N,K", [(16, 3072, 9216), (3, 3072, 12288), (1, 200, 12288)])
 def test_split_k_small_m_is_deterministic_and_reusable(lb, force_variant, fmt, M, N, K):
