@@ -115,6 +115,37 @@ def bench_large(torch, lb, steps, warmup):
                 flop_launch=flop_launch, avg_launch_ms=avg_launch_ms, up_ms=up_ms, down_ms=down_ms)
 
 
+def bench_dense(torch, M, N1, K1, N2, steps=50, warmup=50):
+    """Context: the dense bf16 GEMM that the low-bit layer replaces, through
+    PyTorch's library path (torch.matmul -> hipBLASLt), on the same two shapes
+    (no activation). 2-D contiguous operands only."""
+    g = torch.Generator(device="cuda").manual_seed(11)
+    x = torch.randn((M, K1), generator=g, device="cuda").bfloat16()
+    wu = (torch.randn((K1, N1), generator=g, device="cuda") * 0.02).bfloat16().contiguous()
+    wd = (torch.randn((N1, N2), generator=g, device="cuda") * 0.02).bfloat16().contiguous()
+    h = torch.empty((M, N1), dtype=torch.bfloat16, device="cuda")
+    y = torch.empty((M, N2), dtype=torch.bfloat16, device="cuda")
+    for _ in range(warmup):
+        torch.matmul(x, wu, out=h)
+        torch.matmul(h, wd, out=y)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in evs:
+        e[0].record()
+        torch.matmul(x, wu, out=h)
+        e[1].record()
+        torch.matmul(h, wd, out=y)
+        e[2].record()
+    torch.cuda.synchronize()
+    up = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    down = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    flop = 2.0 * M * N1 * K1
+    return {"what": "torch.matmul (hipBLASLt) with dense bf16 weights on the same two shapes, "
+                    "no activation: the library GEMM the low-bit layer replaces",
+            "up_ms": round(up, 4), "down_ms": round(down, 4),
+            "tflops": round(2 * flop / ((up + down) * 1e-3) / 1e12, 1)}
+
+
 def bench_small(torch, lb, reps=10, fuse_qkv=False):
     """Weight streaming at M = 16 and M = 1 over the 100 ternary linears of one
     transformer pass (and the 1-bit equivalent); with fuse_qkv, the same
@@ -387,6 +418,7 @@ def main():
     tflops = r["flop_step"] / (ms_step * 1e-3) / 1e12
     achieved = r["flop_launch"] / (r["avg_launch_ms"] * 1e-3) / 1e12
     traffic = load_traffic()
+    dense = bench_dense(torch, r["M"], r["N1"], r["K1"], r["N2"])
     small = None if args.no_small else bench_small(torch, lb)
     small_fused = None if args.no_small else bench_small(torch, lb, fuse_qkv=True)
     cpu = None if args.no_cpu else cpu_baseline()
@@ -423,6 +455,7 @@ def main():
             "flop_per_launch": r["flop_launch"],
         },
         "cpu_baseline": cpu,
+        "dense_bf16_matmul": dense,
         "small_m": small,
         "small_m_fused_qkv": small_fused,
     }
