@@ -592,7 +592,7 @@ constexpr int MAXWAVES_CHUNKED = 8;            // several chunks: 512 threads
 }
 
 template <bool BF16, int FMT, int GW, int NCH>
-__global__ __launch_bounds__(64 * (NCH == 1 ? thin::MAXWAVES : thin::MAXWAVES_CHUNKED)) void gemm_thin_kernel(GemmArgs a) {
+__global__ __launch_bounds__(64 * (NCH == 1 ? thin::MAXWAVES : thin::MAXWAVES_CHUNKED)) void gemm_thin_kernel(GemmArgs a, int nch_rt) {
   static_assert(GW == 2 || GW == 4, "two or four groups per chunk");
   constexpr bool TERN = FMT == FMT_TERNARY;
   constexpr int NW = TERN ? GW / 2 : 1;                     // 16-byte code loads per lane and chunk
@@ -609,8 +609,9 @@ __global__ __launch_bounds__(64 * (NCH == 1 ? thin::MAXWAVES : thin::MAXWAVES_CH
   const int nwav = blockDim.x >> 6;
   const int q = lane >> 4, c16 = lane & 15;
   const int G = a.K >> 7;
-  const int g0 = wave * GW * NCH;
-  const int ng = min(GW * NCH, G - g0);                     // 1 .. GW NCH (host plan)
+  const int nch = NCH > 0 ? NCH : nch_rt;                   // chunks per wave (NCH = 0: a runtime count)
+  const int g0 = wave * GW * nch;
+  const int ng = min(GW * nch, G - g0);                     // 1 .. GW nch (host plan)
   const int64_t wrow = TERN ? (a.K >> 2) : (a.K >> 3);
   const float factor = code_factor<TERN>();
   const int n = blockIdx.x * 16 + c16;
@@ -625,9 +626,9 @@ __global__ __launch_bounds__(64 * (NCH == 1 ? thin::MAXWAVES : thin::MAXWAVES_CH
 
   u32x4 cw[NBUF][NW];
   uint32_t sr[NBUF];
-  // issue the loads of chunk c into buffer / register set c % NBUF
-  auto issue = [&](int c) __attribute__((always_inline)) {
-    const int bsel = c % NBUF;
+  // issue the loads of chunk c into buffer / register set bsel (always a
+  // constant at the call site, so the register arrays stay in registers)
+  auto issue = [&](int c, int bsel) __attribute__((always_inline)) {
     uint8_t* xs = xw + bsel * GW * 4096;
 #pragma unroll
     for (int i = 0; i < GW; ++i) {
@@ -654,20 +655,19 @@ __global__ __launch_bounds__(64 * (NCH == 1 ? thin::MAXWAVES : thin::MAXWAVES_CH
     asm volatile("" ::: "memory");                          // keep the chunks' loads in order
   };
 
-  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-  issue(0);
-  if (NCH > 1) issue(1);
-#pragma unroll
-  for (int c = 0; c < NCH; ++c) {
-    const int bsel = c % NBUF;
-    // chunk c has landed (the loads of chunk c+1 may still be in flight)
-    if (c + 1 < NCH) {
+  // wait until the chunk about to be computed has landed: with a later
+  // chunk's loads issued after it (more), only those may stay in flight
+  auto wait_chunk = [&](bool more) __attribute__((always_inline)) {
+    if (more) {
       if (rq == 1) __builtin_amdgcn_s_waitcnt(large::waitcnt_vm(XDMA / 4));
       else if (rq == 2) __builtin_amdgcn_s_waitcnt(large::waitcnt_vm(XDMA / 2));
       else __builtin_amdgcn_s_waitcnt(large::waitcnt_vm(XDMA));
     } else {
       __builtin_amdgcn_s_waitcnt(0);
     }
+  };
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto compute = [&](int c, int bsel) __attribute__((always_inline)) {
     if (c * GW < ng) {                                      // wave-uniform
       // lane exchange (as in the kernel above)
       u32x4 w[NW];
@@ -706,9 +706,31 @@ __global__ __launch_bounds__(64 * (NCH == 1 ? thin::MAXWAVES : thin::MAXWAVES_CH
 #pragma unroll
       for (int u = 0; u < GW; ++u) acc += sc[u] * tmp[u];
     }
-    // chunk c+2 into the buffers of chunk c (this wave's reads of them are
-    // done: their data fed the MFMAs above)
-    if (c + 2 < NCH) issue(c + 2);
+  };
+
+  // chunk c+2 goes into the buffers of chunk c once chunk c is computed
+  // (this wave's reads of them are done: their data fed the MFMAs)
+  issue(0, 0);
+  if (NCH != 1) issue(1, 1);
+  if (NCH > 0) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      wait_chunk(c + 1 < NCH);
+      compute(c, c % NBUF);
+      if (c + 2 < NCH) issue(c + 2, c % NBUF);
+    }
+  } else {
+    // any number of chunks: a loop over pairs, buffer 0 then buffer 1
+    for (int c = 0; c < nch; c += 2) {
+      wait_chunk(c + 1 < nch);
+      compute(c, 0);
+      if (c + 2 < nch) issue(c + 2, 0);
+      if (c + 1 < nch) {
+        wait_chunk(c + 2 < nch);
+        compute(c + 1, 1);
+        if (c + 3 < nch) issue(c + 3, 1);
+      }
+    }
   }
   red[wave][lane] = acc;
   __syncthreads();
@@ -752,11 +774,14 @@ __global__ void gelu_kernel(const void* in, void* out, int dtype, int64_t count)
 // 128 columns, is faster). One chunk per wave (all of the wave's
 // activations in LDS at once) while K allows: GW = 2 with up to 16 waves,
 // else GW = 4 within the LDS (K <= 4608). Longer K: 8 waves, chunks of
-// GW = 2 groups, 3 <= NCH <= 8 chunks per wave, two chunks in flight.
+// GW = 2 groups, NCH >= 3 chunks per wave (compiled for 3 .. 8, a runtime
+// count beyond), two chunks in flight. With any_n the plan is also made for
+// wide N: the fallback when the column-tile plan cannot cover the shape
+// (more than MAXGS * MAXSPLIT groups of K, or too many column tiles).
 struct ThinPlan { int gw, nch, waves, blocks; };
 
-static bool thin_plan(int M, int N, int K, int num_cu, ThinPlan* out) {
-  if (M > 16 || (N + 15) / 16 >= num_cu) return false;
+static bool thin_plan(int M, int N, int K, int num_cu, ThinPlan* out, bool any_n = false) {
+  if (M > 16 || (!any_n && (N + 15) / 16 >= num_cu)) return false;
   const int G = K / 128;
   const int blocks = (N + 15) / 16;
   constexpr size_t LDS = 160 * 1024, RED = 16 * 1024;      // LDS per workgroup, partials
@@ -769,7 +794,6 @@ static bool thin_plan(int M, int N, int K, int num_cu, ThinPlan* out) {
     return true;
   }
   const int nch = (G + 2 * thin::MAXWAVES_CHUNKED - 1) / (2 * thin::MAXWAVES_CHUNKED);
-  if (nch > 8) return false;
   *out = ThinPlan{2, nch, (G + 2 * nch - 1) / (2 * nch), blocks};
   return true;
 }
@@ -823,7 +847,8 @@ bool small_path(int M, int N, int K, int variant) {
   if (variant == 1 || variant == 5 || variant == 6) return false;
   StreamPlan p;
   ThinPlan tp;
-  return (variant != 7 && thin_plan(M, N, K, 256, &tp)) || stream_plan(M, N, K, 256, &p);
+  return (variant != 7 && thin_plan(M, N, K, 256, &tp)) || stream_plan(M, N, K, 256, &p) ||
+         thin_plan(M, N, K, 256, &tp, true);
 }
 
 // Workspace of the small-M kernel when K is split: partials and tickets.
@@ -839,7 +864,7 @@ template <bool BF16, int FMT>
 static void launch_thin_t(const GemmArgs& a, const ThinPlan& p, hipStream_t st) {
   const dim3 grid(p.blocks), block(64 * p.waves);
   const size_t lds = (size_t)p.waves * (p.nch == 1 ? 1 : 2) * p.gw * 4096;
-#define LOWBIT_THIN(GW, NCH) hipLaunchKernelGGL((gemm_thin_kernel<BF16, FMT, GW, NCH>), grid, block, lds, st, a)
+#define LOWBIT_THIN(GW, NCH) hipLaunchKernelGGL((gemm_thin_kernel<BF16, FMT, GW, NCH>), grid, block, lds, st, a, p.nch)
   if (p.nch == 1) {
     if (p.gw == 2) LOWBIT_THIN(2, 1);
     else LOWBIT_THIN(4, 1);
@@ -850,7 +875,8 @@ static void launch_thin_t(const GemmArgs& a, const ThinPlan& p, hipStream_t st) 
       case 5: LOWBIT_THIN(2, 5); break;
       case 6: LOWBIT_THIN(2, 6); break;
       case 7: LOWBIT_THIN(2, 7); break;
-      default: LOWBIT_THIN(2, 8); break;
+      case 8: LOWBIT_THIN(2, 8); break;
+      default: LOWBIT_THIN(2, 0); break;              // runtime chunk count
     }
   }
 #undef LOWBIT_THIN
@@ -933,7 +959,13 @@ hipError_t launch_gemm(int fmt, bool x_bf16, GemmArgs a, int num_cu, int variant
   // 7 = the small-M kernel with the K split across workgroups
   StreamPlan p;
   ThinPlan tp;
-  if (variant != 1 && variant != 5 && variant != 6 && variant != 7 && thin_plan(a.M, a.N, a.K, num_cu, &tp)) {
+  const bool small_ok = variant != 1 && variant != 5 && variant != 6;
+  bool thin = small_ok && variant != 7 && thin_plan(a.M, a.N, a.K, num_cu, &tp);
+  const bool stream = !thin && small_ok && stream_plan(a.M, a.N, a.K, num_cu, &p);
+  // beyond the column-tile plan's reach (very long K, very many columns) the
+  // K-split-inside-the-workgroup kernel takes any N
+  if (!thin && !stream && small_ok) thin = thin_plan(a.M, a.N, a.K, num_cu, &tp, true);
+  if (thin) {
     if (fmt == FMT_TERNARY) {
       if (x_bf16) launch_thin_t<true, FMT_TERNARY>(a, tp, st);
       else launch_thin_t<false, FMT_TERNARY>(a, tp, st);
@@ -941,7 +973,7 @@ hipError_t launch_gemm(int fmt, bool x_bf16, GemmArgs a, int num_cu, int variant
       if (x_bf16) launch_thin_t<true, FMT_BINARY>(a, tp, st);
       else launch_thin_t<false, FMT_BINARY>(a, tp, st);
     }
-  } else if (variant != 1 && variant != 5 && variant != 6 && stream_plan(a.M, a.N, a.K, num_cu, &p)) {
+  } else if (stream) {
     if (fmt == FMT_TERNARY) {
       if (x_bf16) launch_stream_t<true, FMT_TERNARY>(a, p, st);
       else launch_stream_t<false, FMT_TERNARY>(a, p, st);

@@ -216,6 +216,23 @@ def test_large_m_tile_configurations(lb, force_variant, fmt, M, N, K):
     assert not (np.abs(Yg - G) > lim).any()
 
 
+@pytest.mark.parametrize("fmt", ["ternary", "binary"])
+@pytest.mark.parametrize("M,N,K", [(16, 100, 98304), (1, 40, 40960), (3, 4100, 65664)])
+def test_small_m_beyond_the_column_tile_plan(lb, fmt, M, N, K):
+    """M <= 16 with more than 8 chunks of K per wave (runtime chunk count) and,
+    for wide N, more K groups than the column-tile kernel covers (513 > 512):
+    the kernel with the K split inside the workgroup takes both. Checked on
+    sampled columns against the oracle restricted to them."""
+    banner(f"beyond the column-tile plan {fmt} {M}x{N}x{K}")
+    lin = wl.make_linear("beyond", fmt, M, N, K, seed=640 + M, p0=0.35, with_bias=False)
+    Y, _ = run_linear(lin, bias=False)
+    rng = np.random.default_rng(N)
+    cols = np.unique(np.concatenate([np.arange(16), np.arange(N - 16, N), rng.integers(0, N, 32)]))
+    A = oracle.linear(lin.x, lin.x_dtype, lin.codes[cols], lin.scales[cols], None)
+    Mg = oracle.magnitude(lin.x, lin.x_dtype, lin.codes[cols], lin.scales[cols], None)
+    _assert_parity(Y[:, cols], A, Mg, lin.y_dtype, f"{fmt} {M}x{N}x{K}")
+
+
 @pytest.mark.parametrize("M,N,K,ldx", [(4200, 512, 256, 1 << 19),         # large-M kernel, 2 chunks
                                          (16, 8192, 256, 150_000_000),     # column tiles, 2 chunks of 8
                                          (5, 640, 256, 600_000_000)])      # thin kernel, chunks of 3 and 2
