@@ -210,6 +210,56 @@ def bench_small(torch, lb, reps=10, fuse_qkv=False):
     return out
 
 
+def bench_small_single(torch, lb, reps=10, copies=64):
+    """The binary workload's weight-streaming cases: one 1-bit linear of
+    3072 x 3072 and the fused QKV of 9216 x 3072, at M = 16 and M = 1. Each
+    launch reads one of `copies` distinct weight copies (about 75 MB and
+    225 MB in all, so the launches stream from HBM, not from the last-level
+    cache); the launches are captured in a HIP graph and replayed."""
+    import workloads as wl
+    out = {}
+    g = wl.generator(7)
+    gx = wl.generator(8)
+    for (N, K) in ((3072, 3072), (9216, 3072)):
+        c = torch.from_numpy(wl.binary_codes(g, N, K)).cuda()
+        p0 = lb.pack_binary(c)
+        del c
+        s0 = dev16(torch, wl.group_scales(g, N, K), torch.float16)
+        ws_ = [(p0.clone(), s0.clone()) for _ in range(copies)]
+        for M in (16, 1):
+            x = dev16(torch, wl.activations(gx, M, K, "bf16"), torch.bfloat16)
+            y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+            ws = lb.new_workspace(lb.workspace_bytes("binary", M, N, K))
+
+            def run():
+                for p, sc in ws_:
+                    lb.gemm(x, p, sc, "binary", out=y, workspace=ws)
+            run()
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                run()
+            for _ in range(10):
+                graph.replay()
+            torch.cuda.synchronize()
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            t0.record()
+            for _ in range(reps):
+                graph.replay()
+            t1.record()
+            torch.cuda.synchronize()
+            us = t0.elapsed_time(t1) * 1e3 / (reps * copies)
+            nbytes = lb.packed_bytes("binary", N, K) + 2 * N * K // 128 + 2 * M * K + 2 * M * N
+            gbs = nbytes / (us * 1e-6) / 1e9
+            out[f"binary_{N}x{K}_M{M}"] = dict(us_per_launch=round(us, 2), bytes_per_launch=nbytes,
+                                               GBps=round(gbs, 1), frac_hbm_peak=round(gbs / PEAK_HBM_GBS, 4))
+            del graph, x, y, ws
+        del ws_, p0, s0
+        torch.cuda.empty_cache()
+    return out
+
+
 def traffic_probe(torch, lb):
     """Workload for the rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE passes: first a
     plain 256 MiB device copy (calibration: its byte counts are known), then two
@@ -421,6 +471,7 @@ def main():
     dense = bench_dense(torch, r["M"], r["N1"], r["K1"], r["N2"])
     small = None if args.no_small else bench_small(torch, lb)
     small_fused = None if args.no_small else bench_small(torch, lb, fuse_qkv=True)
+    small_single = None if args.no_small else bench_small_single(torch, lb)
     cpu = None if args.no_cpu else cpu_baseline()
     out = {
         "metric": METRIC,
@@ -458,6 +509,7 @@ def main():
         "dense_bf16_matmul": dense,
         "small_m": small,
         "small_m_fused_qkv": small_fused,
+        "small_m_binary_single": small_single,
     }
     print(json.dumps(out), flush=True)
 
