@@ -210,6 +210,68 @@ def bench_small(torch, lb, reps=10, fuse_qkv=False):
     return out
 
 
+def bench_large_sweep(torch, lb, passes=3):
+    """The 100 ternary linears of one transformer pass at M = 4608 tokens, each
+    with its own weights (about 0.7 GB in all); one activation per distinct K
+    and one output buffer per distinct N; one pass after a warm pass, then
+    `passes` timed passes."""
+    import workloads as wl
+    M = 4608
+    shapes = wl.mmdit_linear_shapes()
+    g = wl.generator(4)
+    base = {}
+    for (N, K) in sorted({(N, K) for _, N, K in shapes}):
+        c = torch.from_numpy(wl.ternary_codes(g, N, K, 0.35)).cuda()
+        base[(N, K)] = (lb.pack_ternary(c), dev16(torch, wl.group_scales(g, N, K), torch.float16))
+        del c
+    layers = [(base[(N, K)][0].clone(), base[(N, K)][1].clone(), N, K) for _, N, K in shapes]
+    del base
+    tg = torch.Generator(device="cuda").manual_seed(12)
+    xs = {K: torch.randn((M, K), generator=tg, device="cuda").bfloat16() for K in sorted({K for _, _, K in shapes})}
+    ys = {N: torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for N in sorted({N for _, N, _ in shapes})}
+    ws = lb.new_workspace(max(lb.workspace_bytes("ternary", M, N, K) for _, _, N, K in layers))
+
+    def one_pass():
+        for p, sc, N, K in layers:
+            lb.gemm(xs[K], p, sc, "ternary", out=ys[N], workspace=ws)
+    one_pass()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(passes):
+        one_pass()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / passes
+    flop = sum(2.0 * M * N * K for _, _, N, K in layers)
+    tf = flop / (ms * 1e-3) / 1e12
+    del layers, xs, ys, ws
+    torch.cuda.empty_cache()
+    return dict(M=M, launches=len(shapes), ms_per_pass=round(ms, 3), flop_per_pass=flop,
+                tflops=round(tf, 1), frac_mfma_peak=round(tf / PEAK_BF16_TFLOPS, 4))
+
+
+def hbm_copy(torch, nbytes=1 << 30, reps=10):
+    """Context: a device-to-device copy of 1 GiB (reads and writes counted)."""
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize()
+    gbs = 2.0 * nbytes * reps / (t0.elapsed_time(t1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return dict(bytes_moved_per_copy=2 * nbytes, GBps=round(gbs, 1), frac_hbm_peak=round(gbs / PEAK_HBM_GBS, 4))
+
+
 def bench_small_single(torch, lb, reps=10, copies=64):
     """The binary workload's weight-streaming cases: one 1-bit linear of
     3072 x 3072 and the fused QKV of 9216 x 3072, at M = 16 and M = 1. Each
@@ -469,6 +531,8 @@ def main():
     achieved = r["flop_launch"] / (r["avg_launch_ms"] * 1e-3) / 1e12
     traffic = load_traffic()
     dense = bench_dense(torch, r["M"], r["N1"], r["K1"], r["N2"])
+    sweep = bench_large_sweep(torch, lb)
+    copy = hbm_copy(torch)
     small = None if args.no_small else bench_small(torch, lb)
     small_fused = None if args.no_small else bench_small(torch, lb, fuse_qkv=True)
     small_single = None if args.no_small else bench_small_single(torch, lb)
@@ -507,6 +571,8 @@ def main():
         },
         "cpu_baseline": cpu,
         "dense_bf16_matmul": dense,
+        "large_m_sweep": sweep,
+        "hbm_copy": copy,
         "small_m": small,
         "small_m_fused_qkv": small_fused,
         "small_m_binary_single": small_single,
