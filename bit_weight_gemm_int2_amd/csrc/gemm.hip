@@ -770,7 +770,7 @@ __global__ void gelu_kernel(const void* in, void* out, int dtype, int64_t count)
 
 // Plan of the small-M kernel with the K split inside the workgroup: used
 // only while N / 16 is below the CU count (every workgroup reads all of X
-// from L2; for wider N the kernel above, with X shared through LDS by 64 or
+// from L2; for wider N the kernel above, with X shared through LDS by 48 to
 // 128 columns, is faster). One chunk per wave (all of the wave's
 // activations in LDS at once) while K allows: GW = 2 with up to 16 waves,
 // else GW = 4 within the LDS (K <= 4608). Longer K: 8 waves, chunks of
