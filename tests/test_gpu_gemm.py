@@ -217,6 +217,25 @@ def test_large_m_tile_configurations(lb, force_variant, fmt, M, N, K):
 
 
 @pytest.mark.parametrize("fmt", ["ternary", "binary"])
+@pytest.mark.parametrize("variant,M,N,K", [(None, 5, 520, 2048),           # K split inside the workgroup
+                                           (None, 16, 8192, 1024),         # column tiles
+                                           ("small-split", 7, 3072, 9216),  # K split across workgroups
+                                           (None, 3, 100, 40960)])         # runtime chunk count
+def test_small_m_bias_gelu_epilogue(lb, force_variant, fmt, variant, M, N, K):
+    """fp16 activations, fp16 bias and the fused exact-erf GELU to FP32
+    outputs through each small-M path (bias and GELU are applied once, to the
+    full FP32 sum, also after the cross-workgroup combine)."""
+    force_variant(variant)
+    lin = wl.make_linear("epi", fmt, M, N, K, x_dtype="f16", seed=660 + M, p0=0.35, with_bias=True)
+    A, Mg = oracle_linear(lin)
+    Yg, _ = run_linear(lin, activation="gelu", out_dtype=torch.float32)
+    G = oracle.gelu(A)
+    lim = 1.13 * (oracle.REL_TOL * Mg + oracle.ABS_TOL) + 4 * oracle.ulp(G, "f32")
+    bad = np.abs(Yg - G) > lim
+    assert not bad.any(), f"{int(bad.sum())} outputs outside the bound"
+
+
+@pytest.mark.parametrize("fmt", ["ternary", "binary"])
 @pytest.mark.parametrize("M,N,K", [(16, 100, 98304), (1, 40, 40960), (3, 4100, 65664)])
 def test_small_m_beyond_the_column_tile_plan(lb, fmt, M, N, K):
     """M <= 16 with more than 8 chunks of K per wave (runtime chunk count) and,
