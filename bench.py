@@ -492,6 +492,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-small", action="store_true")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the context runs that launch the same kernels as the timed paths "
+                         "(the 100-linear pass at M = 4608, the single binary linears) and the "
+                         "device copy, so that kernel traces and counters cover the timed paths only")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run the counter-calibration workload instead of the benchmark")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -531,11 +535,11 @@ def main():
     achieved = r["flop_launch"] / (r["avg_launch_ms"] * 1e-3) / 1e12
     traffic = load_traffic()
     dense = bench_dense(torch, r["M"], r["N1"], r["K1"], r["N2"])
-    sweep = bench_large_sweep(torch, lb)
-    copy = hbm_copy(torch)
+    sweep = None if args.no_context else bench_large_sweep(torch, lb)
+    copy = None if args.no_context else hbm_copy(torch)
     small = None if args.no_small else bench_small(torch, lb)
     small_fused = None if args.no_small else bench_small(torch, lb, fuse_qkv=True)
-    small_single = None if args.no_small else bench_small_single(torch, lb)
+    small_single = None if (args.no_small or args.no_context) else bench_small_single(torch, lb)
     cpu = None if args.no_cpu else cpu_baseline()
     out = {
         "metric": METRIC,
