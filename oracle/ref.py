@@ -28,6 +28,11 @@ Readings where the pages are silent (each is listed in the design notes):
   h in {0, 1}) sits at bits [16h + 2i, 16h + 2i + 1]. Even k fill the low half
   word, odd k the high half word. Binary: word ``u`` holds k = 32u .. 32u+31; the
   bit of k = 32u + 2i + h (i in 0..15) sits at bit 16h + i; bit 1 means +1.
+* Base-3 storage (five ternary values per byte, the form that approaches the
+  information rate the pages quote): digit ``d = t + 1``, byte ``j`` holds
+  k = 5j .. 5j+4 with ``d[5j]`` least significant, rows of ceil(K/5) bytes; bytes
+  243 .. 255 are invalid. The pages print no such layout; see the section
+  "Base-3 storage" below.
 * Groups run along K inside one output row; K must be a multiple of 128.
 * The bias, when present, is added once in the output row sum.
 * Output cast: round to nearest, ties to even.
@@ -194,7 +199,91 @@ def unpack_binary(packed: np.ndarray, K: int) -> np.ndarray:
     return t
 
 
+# ---------------------------------------------------------------------------
+# Base-3 storage: five ternary values per byte (the information-rate form)
+# ---------------------------------------------------------------------------
+#
+# The pages price a ternary value at its information content, log2(3) ~ 1.585
+# bits, and quote about 1.71 bits per weight with the group scale (page "Cómo
+# Bonsai Ternary 4B revoluciona la difusión texto-imagen", section
+# "Representación y almacenamiento de los pesos ternarios"; page "Introducing
+# 1-bit and Ternary Bonsai Image 4B", section "量化数学"), while the deployment
+# they describe stores 2 bits per value. Five values fit one byte (3^5 = 243 <=
+# 256), 1.6 bits per weight. The pages do not print a layout; this library's
+# reading:
+# * digit d = t + 1 in {0, 1, 2};
+# * byte j of row n holds k = 5j .. 5j+4 as the base-3 number with d[5j] as its
+#   least significant digit: byte = sum_i d[5j+i] * 3^i;
+# * a row is ceil(K/5) bytes, rows back to back; the last byte of a row holds the
+#   K mod 5 leftover values (when K mod 5 != 0) and no further digits;
+# * a byte of value 243 .. 255 is invalid: its weights decode to 0 and count.
+
+def _base3_digits_per_row(K: int) -> int:
+    return (K + 4) // 5
+
+
+def pack_base3(t: np.ndarray) -> np.ndarray:
+    """int8 codes [N, K] in {-1,0,+1} -> uint8 [N, ceil(K/5)] (five per byte)."""
+    t = np.asarray(t)
+    N, K = t.shape
+    if K < 1:
+        raise ValueError("K must be >= 1")
+    if not np.isin(t, (-1, 0, 1)).all():
+        raise ValueError("ternary codes must lie in {-1, 0, +1}")
+    nb = _base3_digits_per_row(K)
+    d = np.zeros((N, 5 * nb), dtype=np.int64)
+    d[:, :K] = t.astype(np.int64) + 1
+    out = np.zeros((N, nb), dtype=np.int64)
+    for i in range(5):                     # digit i of every byte: k = 5j + i
+        out += d[:, i::5] * 3 ** i
+    return out.astype(np.uint8)
+
+
+def unpack_base3(packed: np.ndarray, K: int) -> Tuple[np.ndarray, int]:
+    """uint8 [N, ceil(K/5)] -> (int8 codes [N, K], number of weights in invalid bytes)."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    N = packed.shape[0]
+    nb = _base3_digits_per_row(K)
+    if packed.shape != (N, nb):
+        raise ValueError("base-3 rows must be ceil(K/5) bytes")
+    v = packed.astype(np.int64)
+    bad = v >= 243
+    t = np.zeros((N, 5 * nb), dtype=np.int8)
+    for i in range(5):
+        digit = (v // 3 ** i) % 3
+        t[:, i::5] = np.where(bad, 0, digit - 1)
+    badk = np.repeat(bad, 5, axis=1)[:, :K]
+    return t[:, :K].copy(), int(badk.sum())
+
+
+def _int2_words(c: np.ndarray) -> np.ndarray:
+    """2-bit codes [N, K] (K % 16 == 0) -> uint8 [N, K/4] in the INT2 word layout."""
+    N, K = c.shape
+    c = c.astype(np.uint32)
+    words = np.zeros((N, K // 16), dtype=np.uint32)
+    for j in range(16):
+        i, h = divmod(j, 2)
+        words |= c[:, j::16] << np.uint32(16 * h + 2 * i)
+    return words.astype("<u4").view(np.uint8).reshape(N, K // 4)
+
+
+def base3_to_ternary(packed: np.ndarray, K: int) -> Tuple[np.ndarray, int]:
+    """Base-3 rows -> the INT2 packed form of the same codes (K % 16 == 0).
+
+    Weights of an invalid base-3 byte get the INT2 pattern 10, which is itself
+    invalid, so the INT2 unpacker counts them again; the count is returned too."""
+    if K % 16:
+        raise ValueError("the INT2 form needs K % 16 == 0")
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    t, invalid = unpack_base3(packed, K)
+    bad = np.repeat(packed.astype(np.int64) >= 243, 5, axis=1)[:, :K]
+    c = np.where(bad, 2, t.astype(np.int64) & 3)
+    return _int2_words(c), invalid
+
+
 def packed_bytes(fmt: str, N: int, K: int) -> int:
+    if fmt == "base3":
+        return N * _base3_digits_per_row(K)
     return N * K // (4 if fmt == "ternary" else 8)
 
 

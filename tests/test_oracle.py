@@ -108,6 +108,97 @@ def test_pack_rejects_out_of_set_codes():
         oracle.pack_binary(np.zeros((1, 32), dtype=np.int8))
 
 
+# ------------------------------------------------------ base-3 storage ---
+
+def test_base3_pack_hand_literal(golden_dir):
+    g = _golden(golden_dir, "base3_pack.json")
+    t = np.array([g["t"]], dtype=np.int8)
+    assert oracle.pack_base3(t).tobytes().hex() == g["packed_hex"]
+    back, bad = oracle.unpack_base3(oracle.pack_base3(t), t.shape[1])
+    assert bad == 0 and np.array_equal(back, t)
+
+
+def test_base3_every_byte_against_python_base3_parser():
+    """All 3^5 = 243 valid bytes: the packer must agree with Python's own base-3
+    integer parser (int(text, 3)) with the digit of the lowest k written last, and
+    the unpacker with numpy's base_repr."""
+    import itertools
+    seen = set()
+    for ts in itertools.product((-1, 0, 1), repeat=5):
+        t = np.array([ts], dtype=np.int8)
+        b = int(oracle.pack_base3(t)[0, 0])
+        text = "".join(str(v + 1) for v in reversed(ts))     # most significant first
+        assert b == int(text, 3)
+        seen.add(b)
+    assert seen == set(range(243))
+    for b in range(243):
+        text = np.base_repr(b, 3).rjust(5, "0")
+        expect = [int(ch) - 1 for ch in reversed(text)]
+        t, bad = oracle.unpack_base3(np.array([[b]], dtype=np.uint8), 5)
+        assert bad == 0 and list(t[0]) == expect
+
+
+def test_base3_ragged_rows_and_padding():
+    g = wl.generator(13)
+    for N, K in [(1, 1), (2, 2), (3, 3), (1, 4), (4, 5), (3, 7), (5, 128), (2, 3072), (7, 1001)]:
+        t = wl.ternary_codes(g, N, K, 0.35)
+        p = oracle.pack_base3(t)
+        assert p.shape == (N, -(-K // 5)) and p.dtype == np.uint8
+        assert oracle.packed_bytes("base3", N, K) == p.size
+        back, bad = oracle.unpack_base3(p, K)
+        assert bad == 0 and np.array_equal(back, t)
+        r = K % 5
+        if r:   # the last byte holds r digits, so it stays below 3^r
+            assert (p[:, -1].astype(int) < 3 ** r).all()
+    # an all-zero row: every full byte is 11111 in base 3 = 121
+    z = oracle.pack_base3(np.zeros((1, 13), dtype=np.int8))
+    assert list(z[0]) == [121, 121, 1 + 3 + 9]
+
+
+def test_base3_invalid_bytes_decode_to_zero_and_count():
+    p = np.array([[121, 243, 255, 0]], dtype=np.uint8)        # K = 18: last byte holds 3
+    t, bad = oracle.unpack_base3(p, 18)
+    assert bad == 10
+    assert list(t[0, 5:15]) == [0] * 10
+    assert list(t[0, :5]) == [0] * 5 and list(t[0, 15:]) == [-1, -1, -1]
+    p2 = np.array([[0, 0, 250]], dtype=np.uint8)             # K = 12: invalid last byte, 2 weights
+    assert oracle.unpack_base3(p2, 12)[1] == 2
+    with pytest.raises(ValueError):
+        oracle.pack_base3(np.full((1, 5), 2, dtype=np.int8))
+
+
+def test_base3_to_ternary_matches_int2_packing():
+    g = wl.generator(14)
+    for N, K in [(1, 16), (3, 80), (4, 128), (9, 3072), (2, 1008)]:
+        t = wl.ternary_codes(g, N, K, 0.35)
+        int2, bad = oracle.base3_to_ternary(oracle.pack_base3(t), K)
+        assert bad == 0 and np.array_equal(int2, oracle.pack_ternary(t))
+    # an invalid base-3 byte becomes the invalid INT2 pattern 10 at its five weights
+    t = np.zeros((1, 16), dtype=np.int8)
+    p = oracle.pack_base3(t)
+    p[0, 1] = 250                                             # k = 5 .. 9
+    int2, bad = oracle.base3_to_ternary(p, 16)
+    assert bad == 5
+    back, bad2 = oracle.unpack_ternary(int2, 16)
+    assert bad2 == 5 and not back.any()
+    word = int.from_bytes(int2[0].tobytes(), "little")
+    for k in range(16):
+        field = (word >> (16 * (k & 1) + 2 * (k >> 1))) & 3
+        assert field == (2 if 5 <= k <= 9 else 0)
+    with pytest.raises(ValueError):
+        oracle.base3_to_ternary(oracle.pack_base3(np.zeros((1, 20), dtype=np.int8)), 20)
+
+
+def test_base3_storage_rate():
+    # 1.6 bits per ternary value for long rows, plus the 16/128 bits of scale:
+    # within 0.02 of the 1.71 bits per weight the pages print as the ternary rate,
+    # against 2.125 for the INT2 storage.
+    N, K = 3072, 3072
+    bits = (oracle.packed_bytes("base3", N, K) + oracle.scale_bytes(N, K)) * 8 / (N * K)
+    assert abs(bits - 1.71) < 0.02 and bits < 2.125
+    assert oracle.packed_bytes("base3", N, K) == N * 615
+
+
 # -------------------------------------------------------- storage / bits ---
 
 def test_storage_sizes_exact():
