@@ -322,6 +322,75 @@ def bench_small_single(torch, lb, reps=10, copies=64):
     return out
 
 
+def bench_base3_transcode(torch, lb, reps=10):
+    """Load-time transcoding of the 100-linear sweep's ternary weights from the
+    base-3 storage (five values per byte) to the INT2 form the GEMM reads
+    (0.57 GB read, 0.71 GB written per pass). Two ways a loader can issue it:
+    one base3_to_int2 launch per linear, each on its own buffers (100 launches,
+    2.5-15 MB each, captured in a HIP graph and replayed), and one launch per
+    distinct K over the rows of every linear with that K stored back to back
+    (3 launches; rows are independent, so this is the same transcoding)."""
+    import workloads as wl
+    shapes = wl.mmdit_linear_shapes()
+    g = wl.generator(9)
+    base = {}
+    for (N, K) in sorted({(N, K) for _, N, K in shapes}):
+        c = torch.from_numpy(wl.ternary_codes(g, N, K, 0.35)).cuda()
+        base[(N, K)] = lb.pack_base3(c)
+        del c
+    ins = [(base[(N, K)].clone(), N, K) for _, N, K in shapes]
+    del base
+    outs = [torch.empty((N, K // 4), dtype=torch.uint8, device="cuda") for _, N, K in ins]
+    rd = sum(lb.packed_bytes("base3", N, K) for _, N, K in ins)
+    wr = sum(lb.packed_bytes("ternary", N, K) for _, N, K in ins)
+
+    def timed(one_pass):
+        one_pass()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            one_pass()
+        for _ in range(5):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            graph.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / reps
+        gbs = (rd + wr) / (ms * 1e-3) / 1e9
+        del graph
+        return ms, gbs
+
+    def per_linear():
+        for (p, N, K), o in zip(ins, outs):
+            lb.base3_to_int2(p, K, check=False, out=o)
+    ms1, gbs1 = timed(per_linear)
+    del outs
+    # the same rows grouped by K, each group one contiguous matrix
+    stacked = {}
+    for K in sorted({K for _, _, K in ins}):
+        rows = [p for p, _, k in ins if k == K]
+        stacked[K] = torch.cat(rows, 0)
+    del ins
+    souts = {K: torch.empty((p.shape[0], K // 4), dtype=torch.uint8, device="cuda") for K, p in stacked.items()}
+
+    def per_k():
+        for K, p in stacked.items():
+            lb.base3_to_int2(p, K, check=False, out=souts[K])
+    ms3, gbs3 = timed(per_k)
+    del stacked, souts
+    torch.cuda.empty_cache()
+    return dict(bytes_read=rd, bytes_written=wr,
+                per_linear=dict(launches=len(shapes), ms_per_pass=round(ms1, 4), GBps=round(gbs1, 1),
+                                frac_hbm_peak=round(gbs1 / PEAK_HBM_GBS, 4)),
+                per_k=dict(launches=3, ms_per_pass=round(ms3, 4), GBps=round(gbs3, 1),
+                           frac_hbm_peak=round(gbs3 / PEAK_HBM_GBS, 4)))
+
+
 def traffic_probe(torch, lb):
     """Workload for the rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE passes: first a
     plain 256 MiB device copy (calibration: its byte counts are known), then two
@@ -451,6 +520,25 @@ def stats_table(stats_csv: str, limit: int = 12) -> str:
     return "\n".join(out)
 
 
+def dispatch_table(trace_csv: str, kernel: str) -> str:
+    """Markdown table of the dispatches of one kernel in a rocprofv3
+    --kernel-trace kernel_trace.csv, grouped by grid size (threads)."""
+    import csv
+    groups = {}
+    for r in csv.DictReader(open(trace_csv)):
+        if kernel not in r["Kernel_Name"]:
+            continue
+        d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        groups.setdefault(int(r["Grid_Size_X"]), []).append(d)
+    out = ["| grid (threads) | workgroups | dispatches | average us | min us | max us |",
+           "|---|---|---|---|---|---|"]
+    for grid in sorted(groups):
+        ds = groups[grid]
+        out.append("| {} | {} | {} | {:.2f} | {:.2f} | {:.2f} |".format(
+            grid, grid // 256, len(ds), sum(ds) / len(ds), min(ds), max(ds)))
+    return "\n".join(out)
+
+
 def cpu_baseline(seconds_target=10.0):
     """The oracle as it stands (float64 dequantise + BLAS matmul) on a bounded
     sample of the step: the first R rows of the MLP pair (R grown up to all 4608),
@@ -500,6 +588,8 @@ def main():
                     help="run the counter-calibration workload instead of the benchmark")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM traffic summary from the two counter runs and exit")
+    ap.add_argument("--dispatch-table", nargs=2, metavar=("TRACE_CSV", "KERNEL"),
+                    help="print one kernel's dispatches from a rocprofv3 kernel_trace.csv by grid size")
     ap.add_argument("--stats-table", metavar="STATS_CSV",
                     help="print a rocprofv3 kernel_stats.csv as a markdown table and exit")
     ap.add_argument("--counter-table", nargs="+", metavar="COUNTER_CSV",
@@ -510,6 +600,9 @@ def main():
         return
     if args.traffic_summary:
         print(json.dumps(traffic_summary(*args.traffic_summary)))
+        return
+    if args.dispatch_table:
+        print(dispatch_table(*args.dispatch_table))
         return
     if args.stats_table:
         print(stats_table(args.stats_table))
@@ -540,6 +633,7 @@ def main():
     small = None if args.no_small else bench_small(torch, lb)
     small_fused = None if args.no_small else bench_small(torch, lb, fuse_qkv=True)
     small_single = None if (args.no_small or args.no_context) else bench_small_single(torch, lb)
+    base3 = None if args.no_small else bench_base3_transcode(torch, lb)
     cpu = None if args.no_cpu else cpu_baseline()
     out = {
         "metric": METRIC,
@@ -580,6 +674,7 @@ def main():
         "small_m": small,
         "small_m_fused_qkv": small_fused,
         "small_m_binary_single": small_single,
+        "base3_to_int2_sweep": base3,
     }
     print(json.dumps(out), flush=True)
 

@@ -21,11 +21,12 @@ LIB_PATH = os.path.join(HERE, "liblowbit.so")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_GROUP, ERR_WORKSPACE, ERR_DEVICE, ERR_HIP = range(9)
 F16, BF16, F32, NONE = 0, 1, 2, 3
-BINARY, TERNARY = 1, 2
+BINARY, TERNARY, BASE3 = 1, 2, 3
 ACT_NONE, ACT_GELU = 0, 1
 GROUP = 128
 
-_FMT = {"ternary": TERNARY, "binary": BINARY, TERNARY: TERNARY, BINARY: BINARY}
+_FMT = {"ternary": TERNARY, "binary": BINARY, "base3": BASE3, TERNARY: TERNARY, BINARY: BINARY,
+        BASE3: BASE3}
 _DT = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
 _ACT = {None: ACT_NONE, "none": ACT_NONE, "gelu": ACT_GELU, ACT_NONE: ACT_NONE, ACT_GELU: ACT_GELU}
 
@@ -41,7 +42,9 @@ SIGNATURES = [
     ("lowbit_scale_count", _I64, [_I64, _I64, _I32]),
     ("pack_ternary", _I32, [_P, _I64, _I64, _P, _P, _P]),
     ("pack_binary", _I32, [_P, _I64, _I64, _P, _P, _P]),
+    ("pack_base3", _I32, [_P, _I64, _I64, _P, _P, _P]),
     ("unpack_lowbit", _I32, [_I32, _P, _I64, _I64, _P, _P, _P]),
+    ("base3_to_int2", _I32, [_P, _I64, _I64, _P, _P, _P]),
     ("lowbit_gemm_workspace_bytes", _SZ, [_I32, _I64, _I64, _I64]),
     ("lowbit_gemm", _I32, [_I32, _P, _I32, _I64, _I64, _I64, _P, _P, _I32, _I64,
                            _P, _I32, _P, _I32, _I64, _I32, _P, _SZ, _P]),
@@ -122,34 +125,63 @@ def _shared_workspace(device: torch.device, nbytes: int) -> torch.Tensor:
     return ws
 
 
-def _pack(fn, codes: torch.Tensor, div: int, check: bool, stream) -> torch.Tensor:
+def _row_bytes(fmt: int, K: int) -> int:
+    return (K + 4) // 5 if fmt == BASE3 else K // (4 if fmt == TERNARY else 8)
+
+
+def _counted(fn, src: torch.Tensor, N: int, K: int, out: torch.Tensor, check: bool, stream, what: str):
+    cnt = torch.empty(1, dtype=torch.int32, device=src.device) if check else None
+    _check(fn(src.data_ptr(), N, K, out.data_ptr(), _ptr(cnt), _stream(stream)), fn.__name__)
+    if check:
+        bad = int(cnt.item())
+        if bad:
+            raise ValueError(f"{bad} {what}")
+    return out
+
+
+def _pack(fn, codes: torch.Tensor, fmt: int, check: bool, stream) -> torch.Tensor:
     _cuda(codes, "codes")
     if codes.dtype != torch.int8 or codes.dim() != 2:
         raise ValueError("codes must be a 2-D int8 tensor")
     codes = codes.contiguous()
     N, K = codes.shape
-    out = torch.empty((N, K // div), dtype=torch.uint8, device=codes.device)
-    cnt = torch.empty(1, dtype=torch.int32, device=codes.device) if check else None
-    _check(fn(codes.data_ptr(), N, K, out.data_ptr(), _ptr(cnt), _stream(stream)), fn.__name__)
-    if check:
-        bad = int(cnt.item())
-        if bad:
-            raise ValueError(f"{bad} code(s) outside the allowed set")
-    return out
+    out = torch.empty((N, _row_bytes(fmt, K)), dtype=torch.uint8, device=codes.device)
+    return _counted(fn, codes, N, K, out, check, stream, "code(s) outside the allowed set")
 
 
 def pack_ternary(codes: torch.Tensor, check: bool = True, stream=None) -> torch.Tensor:
     """int8 codes [N, K] in {-1,0,+1} -> packed uint8 [N, K/4] (K % 16 == 0)."""
-    return _pack(lib().pack_ternary, codes, 4, check, stream)
+    return _pack(lib().pack_ternary, codes, TERNARY, check, stream)
 
 
 def pack_binary(codes: torch.Tensor, check: bool = True, stream=None) -> torch.Tensor:
     """int8 codes [N, K] in {-1,+1} -> packed uint8 [N, K/8] (K % 32 == 0)."""
-    return _pack(lib().pack_binary, codes, 8, check, stream)
+    return _pack(lib().pack_binary, codes, BINARY, check, stream)
+
+
+def pack_base3(codes: torch.Tensor, check: bool = True, stream=None) -> torch.Tensor:
+    """int8 codes [N, K] in {-1,0,+1} -> base-3 uint8 [N, ceil(K/5)] (any K >= 1)."""
+    return _pack(lib().pack_base3, codes, BASE3, check, stream)
+
+
+def base3_to_int2(packed: torch.Tensor, K: int, check: bool = True, out: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    """base-3 uint8 [N, ceil(K/5)] -> INT2 uint8 [N, K/4] for gemm (K % 16 == 0).
+    With check, waits for the device and raises on invalid base-3 bytes."""
+    _cuda(packed, "packed")
+    if packed.dtype != torch.uint8 or packed.dim() != 2 or packed.shape[1] != (K + 4) // 5:
+        raise ValueError("packed must be a 2-D uint8 tensor of ceil(K/5) bytes per row")
+    packed = packed.contiguous()
+    N = packed.shape[0]
+    if out is None:
+        out = torch.empty((N, K // 4), dtype=torch.uint8, device=packed.device)
+    elif out.dtype != torch.uint8 or tuple(out.shape) != (N, K // 4) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous uint8 tensor [N, K/4]")
+    return _counted(lib().base3_to_int2, packed, N, K, out, check, stream, "invalid base-3 value(s)")
 
 
 def unpack(fmt, packed: torch.Tensor, K: int, stream=None) -> Tuple[torch.Tensor, int]:
-    """packed [N, K/4 or K/8] -> (int8 codes [N, K], number of invalid codes)."""
+    """packed [N, K/4, K/8 or ceil(K/5)] -> (int8 codes [N, K], number of invalid codes)."""
     _cuda(packed, "packed")
     packed = packed.contiguous()
     N = packed.shape[0]

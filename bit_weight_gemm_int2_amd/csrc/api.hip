@@ -17,6 +17,8 @@ hipError_t launch_pack(int fmt, const int8_t* codes, int64_t N, int64_t K, uint8
                        int32_t* counter, hipStream_t st);
 hipError_t launch_unpack(int fmt, const uint8_t* packed, int64_t N, int64_t K, int8_t* codes,
                          int32_t* counter, hipStream_t st);
+hipError_t launch_base3_to_int2(const uint8_t* base3, int64_t N, int64_t K, uint8_t* int2,
+                                int32_t* counter, hipStream_t st);
 hipError_t launch_gemm(int fmt, bool x_bf16, GemmArgs a, int num_cu, int variant, hipStream_t st);
 hipError_t launch_gelu(const void* in, void* out, int dtype, int64_t count, hipStream_t st);
 size_t small_workspace_bytes(int M, int N, int K, int num_cu, int variant);
@@ -102,12 +104,19 @@ int64_t lowbit_packed_bytes(int32_t format, int64_t N, int64_t K) {
   if (N < 1 || K < 1 || N >= kMaxDim || K >= kMaxDim) return -1;
   if (format == LOWBIT_TERNARY_INT2) return K % 16 ? -1 : N * (K / 4);
   if (format == LOWBIT_BINARY_1BIT) return K % 32 ? -1 : N * (K / 8);
+  if (format == LOWBIT_TERNARY_BASE3) return N * ((K + 4) / 5);
   return -1;
 }
 
 int64_t lowbit_scale_count(int64_t N, int64_t K, int32_t group) {
   if (group != LOWBIT_GROUP || N < 1 || K < 1 || K % group) return -1;
   return N * (K / group);
+}
+
+static int kernel_format(int32_t format) {
+  return format == LOWBIT_TERNARY_INT2 ? lowbit::FMT_TERNARY
+       : format == LOWBIT_BINARY_1BIT  ? lowbit::FMT_BINARY
+                                       : lowbit::FMT_BASE3;
 }
 
 static int32_t pack_common(int fmt, const int8_t* codes, int64_t N, int64_t K, uint8_t* packed,
@@ -118,8 +127,8 @@ static int32_t pack_common(int fmt, const int8_t* codes, int64_t N, int64_t K, u
     return LOWBIT_ERR_ALIGN;
   int32_t st = current_device(nullptr);
   if (st) return st;
-  hipError_t e = lowbit::launch_pack(fmt == LOWBIT_TERNARY_INT2 ? lowbit::FMT_TERNARY : lowbit::FMT_BINARY,
-                                     codes, N, K, packed, invalid_count, (hipStream_t)stream);
+  hipError_t e = lowbit::launch_pack(kernel_format(fmt), codes, N, K, packed, invalid_count,
+                                     (hipStream_t)stream);
   return e == hipSuccess ? LOWBIT_OK : LOWBIT_ERR_HIP;
 }
 
@@ -133,17 +142,35 @@ int32_t pack_binary(const int8_t* codes, int64_t N, int64_t K, uint8_t* packed,
   return pack_common(LOWBIT_BINARY_1BIT, codes, N, K, packed, invalid_count, stream);
 }
 
+int32_t pack_base3(const int8_t* codes, int64_t N, int64_t K, uint8_t* packed,
+                   int32_t* invalid_count, void* stream) {
+  return pack_common(LOWBIT_TERNARY_BASE3, codes, N, K, packed, invalid_count, stream);
+}
+
 int32_t unpack_lowbit(int32_t format, const uint8_t* packed, int64_t N, int64_t K, int8_t* codes,
                       int32_t* invalid_count, void* stream) {
-  if (format != LOWBIT_TERNARY_INT2 && format != LOWBIT_BINARY_1BIT) return LOWBIT_ERR_DTYPE;
+  if (format != LOWBIT_TERNARY_INT2 && format != LOWBIT_BINARY_1BIT && format != LOWBIT_TERNARY_BASE3)
+    return LOWBIT_ERR_DTYPE;
   if (!codes || !packed) return LOWBIT_ERR_NULL;
   if (lowbit_packed_bytes(format, N, K) < 0) return LOWBIT_ERR_SHAPE;
   if (!aligned(codes, 16) || !aligned(packed, 16) || (invalid_count && !aligned(invalid_count, 4)))
     return LOWBIT_ERR_ALIGN;
   int32_t st = current_device(nullptr);
   if (st) return st;
-  hipError_t e = lowbit::launch_unpack(format == LOWBIT_TERNARY_INT2 ? lowbit::FMT_TERNARY : lowbit::FMT_BINARY,
-                                       packed, N, K, codes, invalid_count, (hipStream_t)stream);
+  hipError_t e = lowbit::launch_unpack(kernel_format(format), packed, N, K, codes, invalid_count,
+                                       (hipStream_t)stream);
+  return e == hipSuccess ? LOWBIT_OK : LOWBIT_ERR_HIP;
+}
+
+int32_t base3_to_int2(const uint8_t* base3, int64_t N, int64_t K, uint8_t* int2,
+                      int32_t* invalid_count, void* stream) {
+  if (!base3 || !int2) return LOWBIT_ERR_NULL;
+  if (lowbit_packed_bytes(LOWBIT_TERNARY_INT2, N, K) < 0) return LOWBIT_ERR_SHAPE;
+  if (!aligned(base3, 16) || !aligned(int2, 16) || (invalid_count && !aligned(invalid_count, 4)))
+    return LOWBIT_ERR_ALIGN;
+  int32_t st = current_device(nullptr);
+  if (st) return st;
+  hipError_t e = lowbit::launch_base3_to_int2(base3, N, K, int2, invalid_count, (hipStream_t)stream);
   return e == hipSuccess ? LOWBIT_OK : LOWBIT_ERR_HIP;
 }
 

@@ -14,7 +14,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 enum { DT_F16 = 0, DT_BF16 = 1, DT_F32 = 2, DT_NONE = 3 };
-enum { FMT_BINARY = 1, FMT_TERNARY = 2 };
+enum { FMT_BINARY = 1, FMT_TERNARY = 2, FMT_BASE3 = 3 };
 enum { ACT_NONE = 0, ACT_GELU = 1 };
 
 struct GemmArgs {

@@ -38,6 +38,13 @@
  *  Binary: bit b = 1 means t = +1, 0 means t = -1. Word u holds
  *    k = 32u .. 32u+31; the bit of k = 32u + 2i + h (i = 0..15) sits at
  *    bit 16h + i.
+ *  Base-3 (storage and transport only; lowbit_gemm reads INT2): five ternary
+ *    values per byte. Digit d = t + 1; byte j of a row holds k = 5j .. 5j+4 as
+ *    sum_i d[5j+i] * 3^i (the lowest k is the least significant digit). A row
+ *    is ceil(K/5) bytes with no padding to a word, rows back to back; the last
+ *    byte of a row holds the K mod 5 leftover values when K mod 5 != 0. Bytes
+ *    243 .. 255 are invalid. 1.6 bits per value, the nearest byte-aligned rate
+ *    to the log2(3) ~ 1.585 bits the pages price a ternary value at.
  *  Scales: FP16, shape [N, K/128], row-major; scale[n, g] covers
  *    k = 128g .. 128g+127 of output row n. Any finite value is allowed
  *    (zero and subnormal included); non-finite scales give unspecified results.
@@ -68,7 +75,7 @@ typedef enum {
 } lowbit_status;
 
 typedef enum { LOWBIT_F16 = 0, LOWBIT_BF16 = 1, LOWBIT_F32 = 2, LOWBIT_NONE = 3 } lowbit_dtype;
-typedef enum { LOWBIT_BINARY_1BIT = 1, LOWBIT_TERNARY_INT2 = 2 } lowbit_format;
+typedef enum { LOWBIT_BINARY_1BIT = 1, LOWBIT_TERNARY_INT2 = 2, LOWBIT_TERNARY_BASE3 = 3 } lowbit_format;
 typedef enum { LOWBIT_ACT_NONE = 0, LOWBIT_ACT_GELU_ERF = 1 } lowbit_activation;
 
 /* ABI version of the loaded library (LOWBIT_ABI_VERSION). */
@@ -81,9 +88,9 @@ const char* lowbit_status_string(int32_t status);
  * Optional: every entry point does the same on first use. */
 int32_t lowbit_init(void);
 
-/* Bytes of packed codes for an N x K matrix: N*K/4 (ternary), N*K/8 (binary);
- * -1 for a bad format or a K that breaks the packing rule (ternary K % 16,
- * binary K % 32) or N, K < 1. */
+/* Bytes of packed codes for an N x K matrix: N*K/4 (ternary), N*K/8 (binary),
+ * N*ceil(K/5) (base-3); -1 for a bad format or a K that breaks the packing
+ * rule (ternary K % 16, binary K % 32) or N, K < 1 or >= 2^31. */
 int64_t lowbit_packed_bytes(int32_t format, int64_t N, int64_t K);
 
 /* Number of FP16 scales, N * K / group; -1 if group != 128 or K % group != 0. */
@@ -107,11 +114,34 @@ int32_t pack_ternary(const int8_t* codes, int64_t N, int64_t K, uint8_t* packed,
 int32_t pack_binary(const int8_t* codes, int64_t N, int64_t K, uint8_t* packed,
                     int32_t* invalid_count, void* stream);
 
+/* Pack int8 ternary codes t[N][K] in {-1,0,+1} into the base-3 layout above
+ * (five values per byte: the storage that comes nearest the log2(3)-bit
+ * information rate of "Representacion y almacenamiento de los pesos
+ * ternarios" and of the quantisation arithmetic on the "Introducing 1-bit and
+ * Ternary Bonsai Image 4B" page). packed: N*ceil(K/5) bytes, must not overlap
+ * codes. Any K >= 1. Values outside {-1,0,+1} are counted in invalid_count
+ * and stored as t = 0. Alignment and ownership as pack_ternary. */
+int32_t pack_base3(const int8_t* codes, int64_t N, int64_t K, uint8_t* packed,
+                   int32_t* invalid_count, void* stream);
+
 /* Inverse of the packers: packed (format layout above) -> int8 codes[N][K].
- * Ternary code 10 is invalid: it decodes to 0 and is counted in
- * invalid_count (nullable). Binary has no invalid pattern (count set to 0). */
+ * Ternary code 10 and base-3 bytes 243 .. 255 are invalid: their values
+ * decode to 0 and are counted, one per value, in invalid_count (nullable).
+ * Binary has no invalid pattern (count set to 0). codes and packed are
+ * 16-byte aligned and do not overlap. */
 int32_t unpack_lowbit(int32_t format, const uint8_t* packed, int64_t N, int64_t K,
                       int8_t* codes, int32_t* invalid_count, void* stream);
+
+/* Load-time transcoding of base-3 codes [N rows of ceil(K/5) bytes] into the
+ * INT2 layout [N*K/4 bytes] that lowbit_gemm reads, on the device, so that
+ * weights can be stored and moved at 1.6 bits per value and computed on at
+ * 2. K % 16 == 0 (the INT2 rule). base3 and int2 are 16-byte aligned and do
+ * not overlap. The values of an invalid base-3 byte become the invalid INT2
+ * pattern 10 (which lowbit_gemm reads as t = 0 and unpack_lowbit counts) and
+ * are counted in invalid_count (nullable, one per value). The output is a
+ * pure function of the input. */
+int32_t base3_to_int2(const uint8_t* base3, int64_t N, int64_t K, uint8_t* int2,
+                      int32_t* invalid_count, void* stream);
 
 /* Workspace bytes lowbit_gemm needs for this problem (0 when none). Depends
  * only on (format, M, N, K) and the current device. Non-zero only for
@@ -129,7 +159,9 @@ size_t lowbit_gemm_workspace_bytes(int32_t format, int64_t M, int64_t N, int64_t
  * |bias|) + 1e-5, plus half an output ulp for FP16/BF16 outputs (before the
  * activation; GELU is then applied to the FP32 value).
  *
- *   format      LOWBIT_TERNARY_INT2 or LOWBIT_BINARY_1BIT
+ *   format      LOWBIT_TERNARY_INT2 or LOWBIT_BINARY_1BIT (base-3 weights
+ *               are transcoded first with base3_to_int2; LOWBIT_TERNARY_BASE3
+ *               here gives LOWBIT_ERR_DTYPE)
  *   X           [M][ldx] of x_dtype (LOWBIT_F16 or LOWBIT_BF16); 16-byte
  *               aligned, K <= ldx < 2^31, ldx % 8 == 0. When X spans 4 GiB
  *               or more ((M-1)*ldx*2 + 2K bytes) it is processed in equal row

@@ -29,7 +29,8 @@ def L():
 
 def test_header_declares_expected_entry_points():
     names = _declared()
-    for want in ("pack_ternary", "pack_binary", "unpack_lowbit", "lowbit_gemm",
+    for want in ("pack_ternary", "pack_binary", "pack_base3", "unpack_lowbit", "base3_to_int2",
+                 "lowbit_gemm",
                  "lowbit_gemm_workspace_bytes", "lowbit_packed_bytes", "lowbit_scale_count",
                  "lowbit_status_string", "lowbit_abi_version", "lowbit_init", "lowbit_gelu"):
         assert want in names
@@ -54,6 +55,12 @@ def test_host_only_queries(L):
     assert L.lowbit_packed_bytes(b.TERNARY, 4, 24) == -1       # K % 16
     assert L.lowbit_packed_bytes(b.BINARY, 4, 48) == -1        # K % 32
     assert L.lowbit_packed_bytes(7, 4, 128) == -1
+    # base-3: ceil(K/5) bytes a row, any K >= 1
+    assert L.lowbit_packed_bytes(b.BASE3, 3072, 3072) == 3072 * 615
+    assert L.lowbit_packed_bytes(b.BASE3, 2, 1) == 2
+    assert L.lowbit_packed_bytes(b.BASE3, 5, 7) == 10
+    assert L.lowbit_packed_bytes(b.BASE3, 1, 0) == -1
+    assert L.lowbit_packed_bytes(b.BASE3, 1, 1 << 31) == -1
     assert L.lowbit_scale_count(3072, 9216, 128) == 3072 * 72
     assert L.lowbit_scale_count(3072, 9216, 64) == -1
     for s in range(9):
@@ -74,7 +81,8 @@ def test_argument_errors_before_any_device_work(L):
                              a["group"], a["N"], a["bias"], a["bd"], a["Y"], a["yd"], a["ldy"],
                              a["act"], a["ws"], a["wsb"], None)
 
-    assert call(fmt=3) == b.ERR_DTYPE
+    assert call(fmt=b.BASE3) == b.ERR_DTYPE                   # the GEMM reads INT2 only
+    assert call(fmt=7) == b.ERR_DTYPE
     assert call(xd=b.F32) == b.ERR_DTYPE
     assert call(yd=b.NONE) == b.ERR_DTYPE
     assert call(bd=9) == b.ERR_DTYPE
@@ -104,5 +112,13 @@ def test_argument_errors_before_any_device_work(L):
     assert L.pack_ternary(P, 4, 24, P, None, None) == b.ERR_SHAPE
     assert L.pack_binary(P + 4, 4, 32, P, None, None) == b.ERR_ALIGN
     assert L.unpack_lowbit(5, P, 4, 32, P, None, None) == b.ERR_DTYPE
+    assert L.pack_base3(P, 4, 0, P, None, None) == b.ERR_SHAPE
+    assert L.pack_base3(P, 4, 7, None, None, None) == b.ERR_NULL
+    assert L.pack_base3(P, 4, 7, P, P + 2, None) == b.ERR_ALIGN   # counter not 4-byte aligned
+    assert L.unpack_lowbit(b.BASE3, P, 0, 7, P, None, None) == b.ERR_SHAPE
+    assert L.base3_to_int2(None, 4, 32, P, None, None) == b.ERR_NULL
+    assert L.base3_to_int2(P, 4, 40, P, None, None) == b.ERR_SHAPE       # INT2 needs K % 16
+    assert L.base3_to_int2(P, 4, 32, P + 4, None, None) == b.ERR_ALIGN
+    assert L.base3_to_int2(P + 1, 4, 32, P, None, None) == b.ERR_ALIGN
     assert L.lowbit_gelu(None, P, b.BF16, 10, None) == b.ERR_NULL
     assert L.lowbit_gelu(P, P, b.NONE, 10, None) == b.ERR_DTYPE
