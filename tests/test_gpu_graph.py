@@ -75,3 +75,46 @@ def test_graph_replay_matches_eager(lb, variant, fmt, M, N, K):
             os.environ.pop("LOWBIT_FORCE_VARIANT", None)
         else:
             os.environ["LOWBIT_FORCE_VARIANT"] = old
+
+
+def test_graph_replay_base3_transcode(lb):
+    """base3_to_int2 with its invalid-value counter, captured once and replayed
+    on new base-3 inputs copied in between (some with invalid bytes): every
+    replay must match the oracle, counter included (the counter is cleared by
+    a kernel inside the graph, not by a memset node)."""
+    import oracle
+    banner("graph replay base3_to_int2")
+    N, K = 300, 1008
+    g = wl.generator(902)
+    inputs = []
+    for r in range(4):
+        p = oracle.pack_base3(wl.ternary_codes(g, N, K, 0.35))
+        if r % 2:
+            p[r, 3] = 243 + r
+            p[N - 1, -1] = 255
+        inputs.append(p)
+    p_dev = torch.from_numpy(inputs[0]).cuda()
+    out = torch.empty((N, K // 4), dtype=torch.uint8, device="cuda")
+    cnt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    L = lb.lib()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+
+    def call():
+        return L.base3_to_int2(p_dev.data_ptr(), N, K, out.data_ptr(), cnt.data_ptr(), st.cuda_stream)
+    with torch.cuda.stream(st):
+        assert call() == 0
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=st):
+        assert call() == 0
+    torch.cuda.synchronize()
+    for r, p in enumerate(inputs):
+        p_dev.copy_(torch.from_numpy(p))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref, bad = oracle.base3_to_ternary(p, K)
+        assert np.array_equal(out.cpu().numpy(), ref), f"replay {r}"
+        assert int(cnt.item()) == bad, f"replay {r}"
