@@ -146,16 +146,27 @@ def bench_dense(torch, M, N1, K1, N2, steps=50, warmup=50):
             "tflops": round(2 * flop / ((up + down) * 1e-3) / 1e12, 1)}
 
 
-def bench_small(torch, lb, reps=10, fuse_qkv=False):
+def bench_small(torch, lb, reps=10, fuse_qkv=False, grouped=False):
     """Weight streaming at M = 16 and M = 1 over the 100 ternary linears of one
     transformer pass (and the 1-bit equivalent); with fuse_qkv, the same
     weights with each stream's Q, K, V rows concatenated at load time (80
+    linears); with grouped as well, each double-stream block's image and text
+    linears of one shape (independent of each other) run as one
+    lowbit_gemm_grouped launch, each stream with its own activations (60
     launches). One code matrix is drawn per distinct shape and copied into its
     own device buffer per linear, so every launch streams distinct memory
     (about 0.75 GB ternary, 0.4 GB binary, far above the 256 MB last-level
     cache)."""
     import workloads as wl
+    assert fuse_qkv or not grouped
     shapes = wl.mmdit_linear_shapes(fuse_qkv)
+    # launches: lists of linear indices (an image / text pair of a double-stream block, or one linear)
+    ops = []
+    for i, (name, _, _) in enumerate(shapes):
+        if grouped and ".img." in name:
+            ops.append([i, shapes.index((name.replace(".img.", ".txt."),) + shapes[i][1:])])
+        elif not (grouped and ".txt." in name):
+            ops.append([i])
     distinct = sorted({(N, K) for _, N, K in shapes})
     out = {}
     for fmt in ("ternary", "binary"):
@@ -173,13 +184,25 @@ def bench_small(torch, lb, reps=10, fuse_qkv=False):
         for M in (16, 1):
             xs = {K: dev16(torch, wl.activations(gx, M, K, "bf16"), torch.bfloat16)
                   for K in sorted({K for _, _, K in shapes})}
+            # the text stream's own activations (grouped launches only)
+            xt = {K: dev16(torch, wl.activations(gx, M, K, "bf16"), torch.bfloat16)
+                  for K in sorted({K for _, _, K in shapes})} if grouped else xs
             ys = [torch.empty((M, N), dtype=torch.bfloat16, device="cuda") for _, _, N, _ in layers]
             need = max(lb.workspace_bytes(fmt, M, N, K) for _, _, N, K in layers)
+            if grouped:
+                need = max(need, max(int(lb.lib().lowbit_gemm_grouped_workspace_bytes(
+                    len(op), lb._FMT[fmt], M, layers[op[0]][2], layers[op[0]][3])) for op in ops))
             ws = lb.new_workspace(need)
 
             def sweep():
-                for (p, s, N, K), yy in zip(layers, ys):
-                    lb.gemm(xs[K], p, s, fmt, out=yy, workspace=ws)
+                for op in ops:
+                    if len(op) == 1:
+                        p, s, N, K = layers[op[0]]
+                        lb.gemm(xs[K], p, s, fmt, out=ys[op[0]], workspace=ws)
+                    else:
+                        K = layers[op[0]][3]
+                        lb.gemm_grouped([xs[K], xt[K]], [layers[i][0] for i in op], [layers[i][1] for i in op],
+                                        fmt, outs=[ys[i] for i in op], workspace=ws)
             # the 100 launches are captured once in a HIP graph and replayed,
             # so the host's per-call Python cost is not what gets timed
             sweep()
@@ -203,8 +226,8 @@ def bench_small(torch, lb, reps=10, fuse_qkv=False):
             gbs = (wbytes + io) / (ms * 1e-3) / 1e9
             out[f"{fmt}_M{M}"] = dict(ms_per_pass=round(ms, 4), bytes_per_pass=wbytes + io,
                                       GBps=round(gbs, 1), frac_hbm_peak=round(gbs / PEAK_HBM_GBS, 4),
-                                      launches=len(layers))
-            del ys, xs, ws, graph
+                                      launches=len(ops))
+            del ys, xs, xt, ws, graph
         del layers
         torch.cuda.empty_cache()
     return out
@@ -632,6 +655,7 @@ def main():
     copy = None if args.no_context else hbm_copy(torch)
     small = None if args.no_small else bench_small(torch, lb)
     small_fused = None if args.no_small else bench_small(torch, lb, fuse_qkv=True)
+    small_grouped = None if args.no_small else bench_small(torch, lb, fuse_qkv=True, grouped=True)
     small_single = None if (args.no_small or args.no_context) else bench_small_single(torch, lb)
     base3 = None if args.no_small else bench_base3_transcode(torch, lb)
     cpu = None if args.no_cpu else cpu_baseline()
@@ -673,6 +697,7 @@ def main():
         "hbm_copy": copy,
         "small_m": small,
         "small_m_fused_qkv": small_fused,
+        "small_m_grouped": small_grouped,
         "small_m_binary_single": small_single,
         "base3_to_int2_sweep": base3,
     }

@@ -49,7 +49,11 @@ SIGNATURES = [
     ("lowbit_gemm", _I32, [_I32, _P, _I32, _I64, _I64, _I64, _P, _P, _I32, _I64,
                            _P, _I32, _P, _I32, _I64, _I32, _P, _SZ, _P]),
     ("lowbit_gelu", _I32, [_P, _P, _I32, _I64, _P]),
+    ("lowbit_gemm_grouped", _I32, [_I32, _I32, _P, _I32, _I64, _I64, _I64, _P, _P, _I32, _I64,
+                                   _P, _I32, _P, _I32, _I64, _I32, _P, _SZ, _P]),
+    ("lowbit_gemm_grouped_workspace_bytes", _SZ, [_I32, _I32, _I64, _I64, _I64]),
 ]
+MAX_GROUP = 8
 
 
 class LowbitError(RuntimeError):
@@ -228,6 +232,58 @@ def gemm(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, fmt, bias:
         _stream(stream))
     _check(st, "lowbit_gemm")
     return out
+
+
+def _ptr_array(ptrs):
+    return (ctypes.c_void_p * len(ptrs))(*ptrs)
+
+
+def gemm_grouped(xs, packeds, scales, fmt, biases=None, out_dtype: Optional[torch.dtype] = None,
+                 activation=None, outs=None, workspace: Optional[torch.Tensor] = None,
+                 stream=None):
+    """Several independent linears of one shape in one launch (small M):
+    ys[z] = act(xs[z] W[z]^T + biases[z]). Every x shares shape, dtype and row
+    stride; every packed / scales pair shares shape. Returns the list of outputs."""
+    count = len(xs)
+    if not 1 <= count <= MAX_GROUP or len(packeds) != count or len(scales) != count:
+        raise ValueError(f"1 .. {MAX_GROUP} problems, with one packed and one scales tensor each")
+    if biases is not None and len(biases) != count:
+        raise ValueError("one bias per problem")
+    x0 = xs[0]
+    for t in list(xs) + list(packeds) + list(scales):
+        _cuda(t, "operand")
+    if x0.dim() != 2 or any(x.shape != x0.shape or x.stride() != x0.stride() or x.dtype != x0.dtype for x in xs):
+        raise ValueError("every x must have the shape, stride and dtype of the first")
+    if x0.stride(1) != 1:
+        raise ValueError("x must have unit stride along K")
+    M, K = x0.shape
+    packeds = [p.contiguous() for p in packeds]
+    scales = [s_.contiguous() for s_ in scales]
+    N = packeds[0].shape[0]
+    if any(p.shape != packeds[0].shape for p in packeds) or any(s_.dtype != torch.float16 for s_ in scales):
+        raise ValueError("packed weights of one shape and float16 scales")
+    odt = out_dtype or x0.dtype
+    if outs is None:
+        outs = [torch.empty((M, N), dtype=odt, device=x0.device) for _ in range(count)]
+    bdt = NONE
+    if biases is not None:
+        biases = [b.contiguous() for b in biases]
+        bdt = _DT[biases[0].dtype]
+    need = int(lib().lowbit_gemm_grouped_workspace_bytes(count, _FMT[fmt], M, N, K))
+    if need and workspace is None:
+        workspace = _shared_workspace(x0.device, need)
+    elif need and workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, "
+                         f"lowbit_gemm_grouped needs {need}")
+    st = lib().lowbit_gemm_grouped(
+        count, _FMT[fmt], _ptr_array([x.data_ptr() for x in xs]), _DT[x0.dtype], M, K, x0.stride(0),
+        _ptr_array([p.data_ptr() for p in packeds]), _ptr_array([s_.data_ptr() for s_ in scales]), GROUP, N,
+        None if biases is None else _ptr_array([b.data_ptr() for b in biases]), bdt,
+        _ptr_array([y.data_ptr() for y in outs]), _DT[outs[0].dtype], outs[0].stride(0), _ACT[activation],
+        _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _stream(stream))
+    _check(st, "lowbit_gemm_grouped")
+    return outs
 
 
 def gelu(x: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:

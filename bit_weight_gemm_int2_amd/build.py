@@ -30,25 +30,50 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the library)")
 
 
-def command(out: str = LIB, extra=()) -> list:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    return [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17", "-shared", "-fPIC",
-            "-Wall", "-Wno-unused-function", *DEVICE_FLAGS, *extra, "-o", out, *srcs]
+COMPILE_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+                 *DEVICE_FLAGS]
+
+
+def compile_command(src: str, obj: str, extra=()) -> list:
+    return [hipcc(), *COMPILE_FLAGS, *extra, "-c", src, "-o", obj]
+
+
+def link_command(out: str, objs) -> list:
+    return [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", out, *objs]
+
+
+def _errors(r) -> str:
+    return "\n".join(l for l in (r.stderr or "").splitlines() if "not a recognized feature" not in l)
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source into liblowbit.so (always recompiles)."""
-    tmp = LIB + ".tmp"
-    cmd = command(tmp)
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    errs = "\n".join(l for l in (r.stderr or "").splitlines()
-                     if "not a recognized feature" not in l)
-    if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{errs}")
-    if verbose and errs.strip():
-        print(errs, file=sys.stderr)
+    """Compile every HIP source into liblowbit.so (always recompiles): the
+    sources compile in parallel, then one link."""
+    import tempfile
+    with tempfile.TemporaryDirectory(prefix="lowbit_build_") as tmpdir:
+        cmds = [compile_command(os.path.join(CSRC, src), os.path.join(tmpdir, src + ".o")) for src in SOURCES]
+        procs = []
+        for cmd in cmds:
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True))
+        failed = []
+        for cmd, pr in zip(cmds, procs):
+            out, err = pr.communicate()
+            r = subprocess.CompletedProcess(cmd, pr.returncode, out, err)
+            if r.returncode != 0:
+                failed.append(f"{os.path.basename(cmd[-3])}:\n{_errors(r)}")
+            elif verbose and _errors(r).strip():
+                print(_errors(r), file=sys.stderr)
+        if failed:
+            raise RuntimeError("hipcc failed:\n" + "\n".join(failed))
+        tmp = LIB + ".tmp"
+        cmd = link_command(tmp, [os.path.join(tmpdir, src + ".o") for src in SOURCES])
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc link failed ({r.returncode}):\n{_errors(r)}")
     os.replace(tmp, LIB)
     return LIB
 

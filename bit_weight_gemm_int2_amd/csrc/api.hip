@@ -19,10 +19,11 @@ hipError_t launch_unpack(int fmt, const uint8_t* packed, int64_t N, int64_t K, i
                          int32_t* counter, hipStream_t st);
 hipError_t launch_base3_to_int2(const uint8_t* base3, int64_t N, int64_t K, uint8_t* int2,
                                 int32_t* counter, hipStream_t st);
-hipError_t launch_gemm(int fmt, bool x_bf16, GemmArgs a, int num_cu, int variant, hipStream_t st);
+hipError_t launch_gemm(int fmt, bool x_bf16, GemmArgs a, int num_cu, int variant, hipStream_t st,
+                       const GemmGroup* group = nullptr, int count = 1);
 hipError_t launch_gelu(const void* in, void* out, int dtype, int64_t count, hipStream_t st);
-size_t small_workspace_bytes(int M, int N, int K, int num_cu, int variant);
-bool small_path(int M, int N, int K, int variant);
+size_t small_workspace_bytes(int M, int N, int K, int num_cu, int variant, int count = 1);
+bool small_path(int M, int N, int K, int variant, int count = 1);
 }  // namespace lowbit
 
 namespace {
@@ -183,10 +184,17 @@ size_t lowbit_gemm_workspace_bytes(int32_t format, int64_t M, int64_t N, int64_t
   return lowbit::small_workspace_bytes((int)M, (int)N, (int)K, num_cu, force_variant());
 }
 
-int32_t lowbit_gemm(int32_t format, const void* X, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx,
-                    const uint8_t* W_packed, const void* scales, int32_t group, int64_t N,
-                    const void* bias, int32_t bias_dtype, void* Y, int32_t y_dtype, int64_t ldy,
-                    int32_t activation, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Every host-side check of one problem of lowbit_gemm (all but the
+// workspace and the device). On success *rows_max is the number of X rows
+// whose offsets fit the kernels' 32-bit addressing.
+int32_t check_problem(int32_t format, const void* X, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx,
+                      const uint8_t* W_packed, const void* scales, int32_t group, int64_t N,
+                      const void* bias, int32_t bias_dtype, void* Y, int32_t y_dtype, int64_t ldy,
+                      int32_t activation, int64_t* rows_max) {
   if (format != LOWBIT_TERNARY_INT2 && format != LOWBIT_BINARY_1BIT) return LOWBIT_ERR_DTYPE;
   if (x_dtype != LOWBIT_F16 && x_dtype != LOWBIT_BF16) return LOWBIT_ERR_DTYPE;
   if (y_dtype != LOWBIT_F16 && y_dtype != LOWBIT_BF16 && y_dtype != LOWBIT_F32) return LOWBIT_ERR_DTYPE;
@@ -206,21 +214,20 @@ int32_t lowbit_gemm(int32_t format, const void* X, int32_t x_dtype, int64_t M, i
   // whose offsets fit (below).
   const int64_t wrow = format == LOWBIT_TERNARY_INT2 ? K / 4 : K / 8;
   if (N * wrow > kOffsetSpan) return LOWBIT_ERR_SHAPE;
-  const int64_t rows_max = (kOffsetSpan - 2 * K) / (2 * ldx) + 1;   // rows whose X offsets fit
+  *rows_max = (kOffsetSpan - 2 * K) / (2 * ldx) + 1;   // rows whose X offsets fit
   // a problem with M > 16 keeps every chunk above 16 rows (same kernels and
   // workspace as the whole problem)
-  if (M > 16 && M > rows_max && rows_max < 34) return LOWBIT_ERR_SHAPE;
+  if (M > 16 && M > *rows_max && *rows_max < 34) return LOWBIT_ERR_SHAPE;
   const size_t ysz = y_dtype == LOWBIT_F32 ? 4 : 2;
   if (!aligned(X, 16) || !aligned(W_packed, 16) || !aligned(scales, 2) || !aligned(Y, ysz) || ldx % 8)
     return LOWBIT_ERR_ALIGN;
   if (bias && !aligned(bias, bias_dtype == LOWBIT_F32 ? 4 : 2)) return LOWBIT_ERR_ALIGN;
-  int num_cu = 0;
-  int32_t st = current_device(&num_cu);
-  if (st) return st;
-  size_t need = lowbit_gemm_workspace_bytes(format, M, N, K);
-  if (need && (!workspace || workspace_bytes < need)) return LOWBIT_ERR_WORKSPACE;
-  if (need && !aligned(workspace, 256)) return LOWBIT_ERR_ALIGN;
+  return LOWBIT_OK;
+}
 
+lowbit::GemmArgs make_args(int32_t format, int64_t K, int64_t ldx, const uint8_t* W_packed, const void* scales,
+                           int64_t N, const void* bias, int32_t bias_dtype, int32_t y_dtype, int64_t ldy,
+                           int32_t activation, void* workspace) {
   lowbit::GemmArgs a{};
   a.ldx = ldx;
   a.W = W_packed;
@@ -233,9 +240,16 @@ int32_t lowbit_gemm(int32_t format, const void* X, int32_t x_dtype, int64_t M, i
   a.N = (int)N;
   a.K = (int)K;
   a.ws = (float*)workspace;
-  const int variant = force_variant();
-  // one launch unless X spans 4 GiB or more; then equal row chunks, in order
-  // on the stream (they may share the workspace)
+  (void)format;
+  return a;
+}
+
+// One problem, in one launch unless X spans 4 GiB or more; then equal row
+// chunks, in order on the stream (they may share the workspace).
+int32_t run_problem(int32_t format, const void* X, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx,
+                    lowbit::GemmArgs a, void* Y, int32_t y_dtype, int64_t ldy, int64_t rows_max, int num_cu,
+                    int variant, void* stream) {
+  const size_t ysz = y_dtype == LOWBIT_F32 ? 4 : 2;
   const int64_t nchunks = M <= rows_max ? 1 : (M + rows_max - 1) / rows_max;
   const int64_t chunk = (M + nchunks - 1) / nchunks;
   for (int64_t m0 = 0; m0 < M; m0 += chunk) {
@@ -247,6 +261,95 @@ int32_t lowbit_gemm(int32_t format, const void* X, int32_t x_dtype, int64_t M, i
     if (e != hipSuccess) return LOWBIT_ERR_HIP;
   }
   return LOWBIT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t lowbit_gemm(int32_t format, const void* X, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx,
+                    const uint8_t* W_packed, const void* scales, int32_t group, int64_t N,
+                    const void* bias, int32_t bias_dtype, void* Y, int32_t y_dtype, int64_t ldy,
+                    int32_t activation, void* workspace, size_t workspace_bytes, void* stream) {
+  int64_t rows_max = 0;
+  int32_t st = check_problem(format, X, x_dtype, M, K, ldx, W_packed, scales, group, N, bias, bias_dtype, Y,
+                             y_dtype, ldy, activation, &rows_max);
+  if (st) return st;
+  int num_cu = 0;
+  st = current_device(&num_cu);
+  if (st) return st;
+  size_t need = lowbit_gemm_workspace_bytes(format, M, N, K);
+  if (need && (!workspace || workspace_bytes < need)) return LOWBIT_ERR_WORKSPACE;
+  if (need && !aligned(workspace, 256)) return LOWBIT_ERR_ALIGN;
+  const lowbit::GemmArgs a = make_args(format, K, ldx, W_packed, scales, N, bias, bias_dtype, y_dtype, ldy,
+                                       activation, workspace);
+  return run_problem(format, X, x_dtype, M, K, ldx, a, Y, y_dtype, ldy, rows_max, num_cu, force_variant(), stream);
+}
+
+size_t lowbit_gemm_grouped_workspace_bytes(int32_t count, int32_t format, int64_t M, int64_t N, int64_t K) {
+  if (count < 1 || count > LOWBIT_MAX_GROUP) return 0;
+  const size_t one = lowbit_gemm_workspace_bytes(format, M, N, K);
+  if (count == 1 || M > 16 || (format != LOWBIT_TERNARY_INT2 && format != LOWBIT_BINARY_1BIT)) return one;
+  if (M < 1 || N < 1 || K < 128 || K % 128 || N >= kMaxDim || K >= kMaxDim) return 0;
+  int num_cu = 0;
+  if (current_device(&num_cu)) return 0;
+  const int v = force_variant();
+  const size_t grouped = lowbit::small_path((int)M, (int)N, (int)K, v, count)
+                             ? lowbit::small_workspace_bytes((int)M, (int)N, (int)K, num_cu, v, count)
+                             : 0;
+  // the problems may also run one by one (activations of 4 GiB or more)
+  return std::max(one, grouped);
+}
+
+int32_t lowbit_gemm_grouped(int32_t count, int32_t format, const void* const* X, int32_t x_dtype, int64_t M,
+                            int64_t K, int64_t ldx, const uint8_t* const* W_packed, const void* const* scales,
+                            int32_t group, int64_t N, const void* const* bias, int32_t bias_dtype,
+                            void* const* Y, int32_t y_dtype, int64_t ldy, int32_t activation,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (count < 1 || count > LOWBIT_MAX_GROUP) return LOWBIT_ERR_SHAPE;
+  if (!X || !W_packed || !scales || !Y) return LOWBIT_ERR_NULL;
+  if (!bias && bias_dtype != LOWBIT_NONE) return LOWBIT_ERR_NULL;
+  int64_t rows_max = 0;
+  for (int z = 0; z < count; ++z) {
+    int32_t st = check_problem(format, X[z], x_dtype, M, K, ldx, W_packed[z], scales[z], group, N,
+                               bias ? bias[z] : nullptr, bias_dtype, Y[z], y_dtype, ldy, activation, &rows_max);
+    if (st) return st;
+  }
+  int num_cu = 0;
+  int32_t st = current_device(&num_cu);
+  if (st) return st;
+  size_t need = lowbit_gemm_grouped_workspace_bytes(count, format, M, N, K);
+  if (need && (!workspace || workspace_bytes < need)) return LOWBIT_ERR_WORKSPACE;
+  if (need && !aligned(workspace, 256)) return LOWBIT_ERR_ALIGN;
+  const int variant = force_variant();
+  lowbit::GemmArgs a = make_args(format, K, ldx, W_packed[0], scales[0], N, bias ? bias[0] : nullptr, bias_dtype,
+                                 y_dtype, ldy, activation, workspace);
+  if (count == 1 || M > 16 || M > rows_max) {
+    // one problem, large M (launches big enough on their own), or activations
+    // that need row chunks: one problem after the other on the stream
+    for (int z = 0; z < count; ++z) {
+      a.W = W_packed[z];
+      a.S = (const uint16_t*)scales[z];
+      a.bias = bias ? bias[z] : nullptr;
+      st = run_problem(format, X[z], x_dtype, M, K, ldx, a, Y[z], y_dtype, ldy, rows_max, num_cu, variant, stream);
+      if (st) return st;
+    }
+    return LOWBIT_OK;
+  }
+  lowbit::GemmGroup g{};
+  for (int z = 0; z < count; ++z) {
+    g.X[z] = (const uint16_t*)X[z];
+    g.W[z] = W_packed[z];
+    g.S[z] = (const uint16_t*)scales[z];
+    g.bias[z] = bias ? bias[z] : nullptr;
+    g.Y[z] = Y[z];
+  }
+  a.X = g.X[0];
+  a.Y = g.Y[0];
+  a.M = (int)M;
+  hipError_t e = lowbit::launch_gemm(format == LOWBIT_TERNARY_INT2 ? lowbit::FMT_TERNARY : lowbit::FMT_BINARY,
+                                     x_dtype == LOWBIT_BF16, a, num_cu, variant, (hipStream_t)stream, &g, count);
+  return e == hipSuccess ? LOWBIT_OK : LOWBIT_ERR_HIP;
 }
 
 int32_t lowbit_gelu(const void* in, void* out, int32_t dtype, int64_t count, void* stream) {

@@ -32,6 +32,32 @@ struct GemmArgs {
   float* ws;           // caller workspace (no kernel uses one at present)
 };
 
+// The operands of the problems of one grouped launch: same shapes, types and
+// activation, different buffers; problem z runs as blockIdx.z. Only the
+// small-M kernels take groups.
+constexpr int kMaxGroup = 8;
+struct GemmGroup {
+  const uint16_t* X[kMaxGroup];
+  const uint8_t* W[kMaxGroup];
+  const uint16_t* S[kMaxGroup];
+  const void* bias[kMaxGroup];
+  void* Y[kMaxGroup];
+};
+
+// Point `a` at the operands of problem z (wave-uniform) of a grouped launch.
+__device__ __forceinline__ void select_problem(GemmArgs& a, const GemmGroup& g, int z) {
+#pragma unroll
+  for (int i = 1; i < kMaxGroup; ++i) {
+    if (z == i) {
+      a.X = g.X[i];
+      a.W = g.W[i];
+      a.S = g.S[i];
+      a.bias = g.bias[i];
+      a.Y = g.Y[i];
+    }
+  }
+}
+
 __device__ __forceinline__ float half_bits_to_float(uint16_t h) {
   return (float)__builtin_bit_cast(_Float16, h);
 }

@@ -362,8 +362,11 @@ __device__ __forceinline__ int stream_chunk(int q, int s) {
   return TERN ? ((q & 1) * 8 + (q >> 1) * 2 + (s & 1) + (s >> 1) * 4) : (4 * q + s);
 }
 
-template <bool BF16, int FMT, int WC, int GS>
-__global__ __launch_bounds__(64 * WC * stream::kparts(WC, GS)) void gemm_stream_kernel(GemmArgs a, int splits, int gps) {
+// GRP: a grouped launch (problem blockIdx.z of two or more); compiled
+// separately so that single-problem launches carry no selection code.
+template <bool BF16, int FMT, int WC, int GS, bool GRP>
+__global__ __launch_bounds__(64 * WC * stream::kparts(WC, GS)) void gemm_stream_kernel(GemmArgs a, int splits, int gps, GemmGroup grp) {
+  if constexpr (GRP) select_problem(a, grp, blockIdx.z);
   constexpr bool TERN = FMT == FMT_TERNARY;
   constexpr int KH = stream::kparts(WC, GS), GH = GS / KH;   // K parts, slots per part
   constexpr int NW = TERN ? GH / 2 : (GH + 3) / 4;    // 16-byte code loads per lane
@@ -515,10 +518,12 @@ __global__ __launch_bounds__(64 * WC * stream::kparts(WC, GS)) void gemm_stream_
   }
   // partial tiles, lane-major: [split][tile][wave][lane] x 4 floats, written
   // and read as two 64-bit agent-scope atomics per lane
-  int* ticket = (int*)a.ws + tile;
+  // (the tiles of the problems of a grouped launch side by side)
+  const int wtile = GRP ? blockIdx.z * gridDim.x + tile : tile;
+  int* ticket = (int*)a.ws + wtile;
   uint64_t* part = (uint64_t*)((uint8_t*)a.ws + stream::TICKET_BYTES);
-  const int64_t tile_lanes = (int64_t)gridDim.x * WC * 64;
-  const int64_t my = (int64_t)(tile * WC + cwv) * 64 + lane;
+  const int64_t tile_lanes = (int64_t)gridDim.x * (GRP ? gridDim.z : 1) * WC * 64;
+  const int64_t my = (int64_t)(wtile * WC + cwv) * 64 + lane;
   if (lead) {
     uint64_t* dst = part + 2 * ((int64_t)split * tile_lanes + my);
     __hip_atomic_store(dst, __builtin_bit_cast(uint64_t, f32x2{acc[0], acc[1]}), __ATOMIC_RELAXED,
@@ -591,8 +596,9 @@ constexpr int MAXWAVES = 16;                   // one chunk: 1024 threads, at mo
 constexpr int MAXWAVES_CHUNKED = 8;            // several chunks: 512 threads
 }
 
-template <bool BF16, int FMT, int GW, int NCH>
-__global__ __launch_bounds__(64 * (NCH == 1 ? thin::MAXWAVES : thin::MAXWAVES_CHUNKED)) void gemm_thin_kernel(GemmArgs a, int nch_rt) {
+template <bool BF16, int FMT, int GW, int NCH, bool GRP>
+__global__ __launch_bounds__(64 * (NCH == 1 ? thin::MAXWAVES : thin::MAXWAVES_CHUNKED)) void gemm_thin_kernel(GemmArgs a, int nch_rt, GemmGroup grp) {
+  if constexpr (GRP) select_problem(a, grp, blockIdx.z);
   static_assert(GW == 2 || GW == 4, "two or four groups per chunk");
   constexpr bool TERN = FMT == FMT_TERNARY;
   constexpr int NW = TERN ? GW / 2 : 1;                     // 16-byte code loads per lane and chunk
@@ -778,10 +784,11 @@ __global__ void gelu_kernel(const void* in, void* out, int dtype, int64_t count)
 // count beyond), two chunks in flight. With any_n the plan is also made for
 // wide N: the fallback when the column-tile plan cannot cover the shape
 // (more than MAXGS * MAXSPLIT groups of K, or too many column tiles).
+// A grouped launch of `count` problems counts the blocks of all of them.
 struct ThinPlan { int gw, nch, waves, blocks; };
 
-static bool thin_plan(int M, int N, int K, int num_cu, ThinPlan* out, bool any_n = false) {
-  if (M > 16 || (!any_n && (N + 15) / 16 >= num_cu)) return false;
+static bool thin_plan(int M, int N, int K, int num_cu, ThinPlan* out, bool any_n = false, int count = 1) {
+  if (M > 16 || (!any_n && count * ((N + 15) / 16) >= num_cu)) return false;
   const int G = K / 128;
   const int blocks = (N + 15) / 16;
   constexpr size_t LDS = 160 * 1024, RED = 16 * 1024;      // LDS per workgroup, partials
@@ -811,7 +818,9 @@ struct StreamPlan { int wc, gs, gps, splits, tiles; };
 
 static int round_gs(int g) { return g <= 4 ? 4 : g <= 8 ? 8 : g <= 12 ? 12 : g <= 16 ? 16 : g <= 24 ? 24 : 32; }
 
-static bool stream_plan(int M, int N, int K, int num_cu, StreamPlan* out) {
+// `tiles` is per problem; a grouped launch of `count` problems runs
+// count * tiles column tiles side by side.
+static bool stream_plan(int M, int N, int K, int num_cu, StreamPlan* out, int count = 1) {
   if (M > 16) return false;
   const int G = K / 128;
   if (G > stream::MAXGS * stream::MAXSPLIT) return false;
@@ -819,7 +828,7 @@ static bool stream_plan(int M, int N, int K, int num_cu, StreamPlan* out) {
   StreamPlan bp{};
   for (int wc : {3, 4, 5, 6, 8}) {
   const int tiles = (N + 16 * wc - 1) / (16 * wc);
-  if (tiles > stream::MAXTILES) continue;
+  if ((int64_t)tiles * count > stream::MAXTILES) continue;
   for (int sp = 1; sp <= min(stream::MAXSPLIT, G); ++sp) {
     const int gps = (G + sp - 1) / sp;
     if (gps > stream::MAXGS) continue;
@@ -828,7 +837,7 @@ static bool stream_plan(int M, int N, int K, int num_cu, StreamPlan* out) {
     const int kh = stream::kparts(wc, gs);
     const size_t lds = stream::lds_bytes(gs) + (size_t)kh * wc * 1024;
     const int per_cu = max(1, min((int)(160 * 1024 / lds), 32 / (wc * kh)));
-    const int rounds = (tiles * S + num_cu * per_cu - 1) / (num_cu * per_cu);
+    const int rounds = (tiles * count * S + num_cu * per_cu - 1) / (num_cu * per_cu);
     const double clk = gps * (4096.0 + wc * 16 * 32) / 64.0 + gps * 4 * 40.0 / kh;
     const double us = rounds * clk / 2100.0 + (S > 1 ? 3.0 : 0.0);
     if (us < best) {
@@ -843,28 +852,34 @@ static bool stream_plan(int M, int N, int K, int num_cu, StreamPlan* out) {
 
 // The small-M kernel covers every M <= 16 with N <= 16384 * 128 (unless the
 // large-M kernel is forced).
-bool small_path(int M, int N, int K, int variant) {
+bool small_path(int M, int N, int K, int variant, int count) {
   if (variant == 1 || variant == 5 || variant == 6) return false;
   StreamPlan p;
   ThinPlan tp;
-  return (variant != 7 && thin_plan(M, N, K, 256, &tp)) || stream_plan(M, N, K, 256, &p) ||
-         thin_plan(M, N, K, 256, &tp, true);
+  return (variant != 7 && thin_plan(M, N, K, 256, &tp, false, count)) ||
+         stream_plan(M, N, K, 256, &p, count) || thin_plan(M, N, K, 256, &tp, true, count);
 }
 
 // Workspace of the small-M kernel when K is split: partials and tickets.
-size_t small_workspace_bytes(int M, int N, int K, int num_cu, int variant) {
+size_t small_workspace_bytes(int M, int N, int K, int num_cu, int variant, int count) {
   ThinPlan tp;
-  if (variant != 7 && thin_plan(M, N, K, num_cu, &tp)) return 0;
+  if (variant != 7 && thin_plan(M, N, K, num_cu, &tp, false, count)) return 0;
   StreamPlan p;
-  if (!stream_plan(M, N, K, num_cu, &p) || p.splits == 1) return 0;
-  return stream::TICKET_BYTES + (size_t)p.splits * p.tiles * p.wc * 64 * 4 * sizeof(float);
+  if (!stream_plan(M, N, K, num_cu, &p, count) || p.splits == 1) return 0;
+  return stream::TICKET_BYTES + (size_t)p.splits * count * p.tiles * p.wc * 64 * 4 * sizeof(float);
 }
 
 template <bool BF16, int FMT>
-static void launch_thin_t(const GemmArgs& a, const ThinPlan& p, hipStream_t st) {
-  const dim3 grid(p.blocks), block(64 * p.waves);
+static void launch_thin_t(const GemmArgs& a, const GemmGroup& g, int count, const ThinPlan& p, hipStream_t st) {
+  const dim3 grid(p.blocks, 1, count), block(64 * p.waves);
   const size_t lds = (size_t)p.waves * (p.nch == 1 ? 1 : 2) * p.gw * 4096;
-#define LOWBIT_THIN(GW, NCH) hipLaunchKernelGGL((gemm_thin_kernel<BF16, FMT, GW, NCH>), grid, block, lds, st, a, p.nch)
+#define LOWBIT_THIN(GW, NCH)                                                                              \
+  do {                                                                                                    \
+    if (count > 1)                                                                                        \
+      hipLaunchKernelGGL((gemm_thin_kernel<BF16, FMT, GW, NCH, true>), grid, block, lds, st, a, p.nch, g);  \
+    else                                                                                                  \
+      hipLaunchKernelGGL((gemm_thin_kernel<BF16, FMT, GW, NCH, false>), grid, block, lds, st, a, p.nch, g); \
+  } while (0)
   if (p.nch == 1) {
     if (p.gw == 2) LOWBIT_THIN(2, 1);
     else LOWBIT_THIN(4, 1);
@@ -883,11 +898,19 @@ static void launch_thin_t(const GemmArgs& a, const ThinPlan& p, hipStream_t st) 
 }
 
 template <bool BF16, int FMT>
-static void launch_stream_t(const GemmArgs& a, const StreamPlan& p, hipStream_t st) {
-  const dim3 grid(p.tiles, p.splits), block(64 * p.wc * stream::kparts(p.wc, p.gs));
+static void launch_stream_t(const GemmArgs& a, const GemmGroup& g, int count, const StreamPlan& p,
+                            hipStream_t st) {
+  const dim3 grid(p.tiles, p.splits, count), block(64 * p.wc * stream::kparts(p.wc, p.gs));
   const size_t lds = stream::lds_bytes(p.gs);
-#define LOWBIT_STREAM(WC, GS) \
-  hipLaunchKernelGGL((gemm_stream_kernel<BF16, FMT, WC, GS>), grid, block, lds, st, a, p.splits, p.gps)
+#define LOWBIT_STREAM(WC, GS)                                                                      \
+  do {                                                                                             \
+    if (count > 1)                                                                                 \
+      hipLaunchKernelGGL((gemm_stream_kernel<BF16, FMT, WC, GS, true>), grid, block, lds, st, a,    \
+                         p.splits, p.gps, g);                                                      \
+    else                                                                                           \
+      hipLaunchKernelGGL((gemm_stream_kernel<BF16, FMT, WC, GS, false>), grid, block, lds, st, a,   \
+                         p.splits, p.gps, g);                                                      \
+  } while (0)
 #define LOWBIT_STREAM_GS(WC)             \
   if (p.gs == 4) LOWBIT_STREAM(WC, 4);   \
   else if (p.gs == 8) LOWBIT_STREAM(WC, 8);   \
@@ -953,41 +976,57 @@ static void launch_large_t(const GemmArgs& a, int num_cu, int variant, hipStream
   }
 }
 
-hipError_t launch_gemm(int fmt, bool x_bf16, GemmArgs a, int num_cu, int variant, hipStream_t st) {
+hipError_t launch_gemm(int fmt, bool x_bf16, GemmArgs a, int num_cu, int variant, hipStream_t st,
+                       const GemmGroup* group, int count) {
   // variant: 0 = automatic, 1 = force the large-M kernel, 2 = small-M
   // kernels only (M <= 16), 5 / 6 = large-M kernel with wide / pair tiles,
-  // 7 = the small-M kernel with the K split across workgroups
+  // 7 = the small-M kernel with the K split across workgroups.
+  // group / count: `count` problems of the same shape in one launch of a
+  // small-M kernel (problem 0 is `a`, problem z > 0 takes its buffers from
+  // `group`); the large-M kernel runs them one launch each.
+  GemmGroup g{};
+  if (group) g = *group;
+  if (count < 1) count = 1;
   StreamPlan p;
   ThinPlan tp;
   const bool small_ok = variant != 1 && variant != 5 && variant != 6;
-  bool thin = small_ok && variant != 7 && thin_plan(a.M, a.N, a.K, num_cu, &tp);
-  const bool stream = !thin && small_ok && stream_plan(a.M, a.N, a.K, num_cu, &p);
+  bool thin = small_ok && variant != 7 && thin_plan(a.M, a.N, a.K, num_cu, &tp, false, count);
+  const bool stream = !thin && small_ok && stream_plan(a.M, a.N, a.K, num_cu, &p, count);
   // beyond the column-tile plan's reach (very long K, very many columns) the
   // K-split-inside-the-workgroup kernel takes any N
-  if (!thin && !stream && small_ok) thin = thin_plan(a.M, a.N, a.K, num_cu, &tp, true);
+  if (!thin && !stream && small_ok) thin = thin_plan(a.M, a.N, a.K, num_cu, &tp, true, count);
   if (thin) {
     if (fmt == FMT_TERNARY) {
-      if (x_bf16) launch_thin_t<true, FMT_TERNARY>(a, tp, st);
-      else launch_thin_t<false, FMT_TERNARY>(a, tp, st);
+      if (x_bf16) launch_thin_t<true, FMT_TERNARY>(a, g, count, tp, st);
+      else launch_thin_t<false, FMT_TERNARY>(a, g, count, tp, st);
     } else {
-      if (x_bf16) launch_thin_t<true, FMT_BINARY>(a, tp, st);
-      else launch_thin_t<false, FMT_BINARY>(a, tp, st);
+      if (x_bf16) launch_thin_t<true, FMT_BINARY>(a, g, count, tp, st);
+      else launch_thin_t<false, FMT_BINARY>(a, g, count, tp, st);
     }
   } else if (stream) {
     if (fmt == FMT_TERNARY) {
-      if (x_bf16) launch_stream_t<true, FMT_TERNARY>(a, p, st);
-      else launch_stream_t<false, FMT_TERNARY>(a, p, st);
+      if (x_bf16) launch_stream_t<true, FMT_TERNARY>(a, g, count, p, st);
+      else launch_stream_t<false, FMT_TERNARY>(a, g, count, p, st);
     } else {
-      if (x_bf16) launch_stream_t<true, FMT_BINARY>(a, p, st);
-      else launch_stream_t<false, FMT_BINARY>(a, p, st);
+      if (x_bf16) launch_stream_t<true, FMT_BINARY>(a, g, count, p, st);
+      else launch_stream_t<false, FMT_BINARY>(a, g, count, p, st);
     }
   } else {
-    if (fmt == FMT_TERNARY) {
-      if (x_bf16) launch_large_t<true, FMT_TERNARY>(a, num_cu, variant, st);
-      else launch_large_t<false, FMT_TERNARY>(a, num_cu, variant, st);
-    } else {
-      if (x_bf16) launch_large_t<true, FMT_BINARY>(a, num_cu, variant, st);
-      else launch_large_t<false, FMT_BINARY>(a, num_cu, variant, st);
+    for (int z = 0; z < count; ++z) {
+      if (z > 0) {
+        a.X = g.X[z];
+        a.W = g.W[z];
+        a.S = g.S[z];
+        a.bias = g.bias[z];
+        a.Y = g.Y[z];
+      }
+      if (fmt == FMT_TERNARY) {
+        if (x_bf16) launch_large_t<true, FMT_TERNARY>(a, num_cu, variant, st);
+        else launch_large_t<false, FMT_TERNARY>(a, num_cu, variant, st);
+      } else {
+        if (x_bf16) launch_large_t<true, FMT_BINARY>(a, num_cu, variant, st);
+        else launch_large_t<false, FMT_BINARY>(a, num_cu, variant, st);
+      }
     }
   }
   return hipGetLastError();

@@ -61,6 +61,7 @@ extern "C" {
 
 #define LOWBIT_ABI_VERSION 1
 #define LOWBIT_GROUP 128
+#define LOWBIT_MAX_GROUP 8   /* problems per lowbit_gemm_grouped call */
 
 typedef enum {
   LOWBIT_OK = 0,
@@ -196,6 +197,42 @@ int32_t lowbit_gemm(int32_t format,
                     int32_t activation,
                     void* workspace, size_t workspace_bytes,
                     void* stream);
+
+/* Several independent linears of one shape in one launch: problem z computes
+ *
+ *   Y[z] = act( X[z] W[z]^T + bias[z] )
+ *
+ * exactly as lowbit_gemm would (same accuracy contract and determinism), for
+ * z = 0 .. count-1, 1 <= count <= LOWBIT_MAX_GROUP. Every problem shares
+ * format, dtypes, activation, M, N, K, group, ldx and ldy; X, W_packed,
+ * scales and Y are HOST arrays of count device pointers (each meeting the
+ * rules of lowbit_gemm), and bias is NULL (no bias, bias_dtype
+ * LOWBIT_NONE) or a host array of count device pointers. No Y may overlap
+ * another Y or any input.
+ *
+ * The reason is launch count at small M: the double-stream blocks of the
+ * transformer ("Arquitectura de despliegue y eficiencia en tiempo de
+ * ejecucion": 5 double-stream and 20 single-stream blocks) run the same
+ * linears on an image and a text stream, independent of each other, and at
+ * M <= 16 each launch is bound by its own latency rather than by bytes. For
+ * M <= 16 the problems run as one launch of the small-M kernels, planned over
+ * the column tiles of all of them. For M > 16 (launches big enough on their
+ * own), or activations that lowbit_gemm would split into row chunks, they
+ * run one after the other on the stream.
+ * workspace: lowbit_gemm_grouped_workspace_bytes(count, format, M, N, K)
+ * bytes, with the rules of lowbit_gemm's workspace. */
+int32_t lowbit_gemm_grouped(int32_t count, int32_t format,
+                            const void* const* X, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx,
+                            const uint8_t* const* W_packed, const void* const* scales, int32_t group,
+                            int64_t N, const void* const* bias, int32_t bias_dtype,
+                            void* const* Y, int32_t y_dtype, int64_t ldy,
+                            int32_t activation,
+                            void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* Workspace bytes lowbit_gemm_grouped needs (0 when none); 0 as well for a
+ * count outside 1 .. LOWBIT_MAX_GROUP. */
+size_t lowbit_gemm_grouped_workspace_bytes(int32_t count, int32_t format, int64_t M, int64_t N, int64_t K);
 
 /* Exact-erf GELU, y = x * Phi(x), computed in FP32, elementwise over `count`
  * values of `dtype` (F16, BF16 or F32); in and out may be the same buffer and

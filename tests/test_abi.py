@@ -30,7 +30,7 @@ def L():
 def test_header_declares_expected_entry_points():
     names = _declared()
     for want in ("pack_ternary", "pack_binary", "pack_base3", "unpack_lowbit", "base3_to_int2",
-                 "lowbit_gemm",
+                 "lowbit_gemm", "lowbit_gemm_grouped", "lowbit_gemm_grouped_workspace_bytes",
                  "lowbit_gemm_workspace_bytes", "lowbit_packed_bytes", "lowbit_scale_count",
                  "lowbit_status_string", "lowbit_abi_version", "lowbit_init", "lowbit_gelu"):
         assert want in names
@@ -121,4 +121,24 @@ def test_argument_errors_before_any_device_work(L):
     assert L.base3_to_int2(P, 4, 32, P + 4, None, None) == b.ERR_ALIGN
     assert L.base3_to_int2(P + 1, 4, 32, P, None, None) == b.ERR_ALIGN
     assert L.lowbit_gelu(None, P, b.BF16, 10, None) == b.ERR_NULL
+    # grouped: host arrays of device pointers
+    arr = lambda *ptrs: (ctypes.c_void_p * len(ptrs))(*ptrs)
+
+    def grouped(count=2, X=None, W=None, S=None, Y=None, bias=None, bd=b.NONE, fmt=b.TERNARY, M=16):
+        X = arr(P, P) if X is None else X
+        W = arr(P, P) if W is None else W
+        S = arr(P, P) if S is None else S
+        Y = arr(P, P) if Y is None else Y
+        return L.lowbit_gemm_grouped(count, fmt, X, b.BF16, M, 256, 256, W, S, 128, 64, bias, bd,
+                                     Y, b.BF16, 64, 0, None, 0, None)
+    assert grouped(count=0) == b.ERR_SHAPE
+    assert grouped(count=9) == b.ERR_SHAPE
+    assert grouped(fmt=b.BASE3) == b.ERR_DTYPE
+    assert grouped(Y=arr(P, None)) == b.ERR_NULL                 # one problem's output missing
+    assert grouped(X=arr(P, P + 8)) == b.ERR_ALIGN               # one problem's X misaligned
+    assert grouped(bd=b.F16) == b.ERR_NULL                       # bias dtype without biases
+    assert L.lowbit_gemm_grouped(2, b.TERNARY, None, b.BF16, 16, 256, 256, arr(P, P), arr(P, P), 128, 64,
+                                 None, b.NONE, arr(P, P), b.BF16, 64, 0, None, 0, None) == b.ERR_NULL
+    assert L.lowbit_gemm_grouped_workspace_bytes(0, b.TERNARY, 16, 64, 256) == 0
+    assert L.lowbit_gemm_grouped_workspace_bytes(9, b.TERNARY, 16, 64, 256) == 0
     assert L.lowbit_gelu(P, P, b.NONE, 10, None) == b.ERR_DTYPE
