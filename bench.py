@@ -530,7 +530,7 @@ def counter_table(csvs, num_simd: int = 1024, num_xcd: int = 8) -> str:
     return "\n".join(out)
 
 
-def stats_table(stats_csv: str, limit: int = 12) -> str:
+def stats_table(stats_csv: str, limit: int = 24) -> str:
     """Markdown table of a rocprofv3 --kernel-trace --stats kernel_stats.csv
     (durations converted from ns to us)."""
     import csv
