@@ -295,12 +295,12 @@ def hbm_copy(torch, nbytes=1 << 30, reps=10):
     return dict(bytes_moved_per_copy=2 * nbytes, GBps=round(gbs, 1), frac_hbm_peak=round(gbs / PEAK_HBM_GBS, 4))
 
 
-def bench_small_single(torch, lb, reps=10, copies=64):
+def bench_small_single(torch, lb, reps=5, rotate_bytes=1 << 30):
     """The binary workload's weight-streaming cases: one 1-bit linear of
-    3072 x 3072 and the fused QKV of 9216 x 3072, at M = 16 and M = 1. Each
-    launch reads one of `copies` distinct weight copies (about 75 MB and
-    225 MB in all, so the launches stream from HBM, not from the last-level
-    cache); the launches are captured in a HIP graph and replayed."""
+    3072 x 3072 and the fused QKV of 9216 x 3072, at M = 16 and M = 1. The
+    launches rotate over distinct weight copies totalling at least 1 GiB
+    (four times the 256 MB last-level cache, so each launch streams its
+    weights from HBM); they are captured in a HIP graph and replayed."""
     import workloads as wl
     out = {}
     g = wl.generator(7)
@@ -310,6 +310,8 @@ def bench_small_single(torch, lb, reps=10, copies=64):
         p0 = lb.pack_binary(c)
         del c
         s0 = dev16(torch, wl.group_scales(g, N, K), torch.float16)
+        per_copy = p0.numel() + 2 * s0.numel()
+        copies = -(-rotate_bytes // per_copy)
         ws_ = [(p0.clone(), s0.clone()) for _ in range(copies)]
         for M in (16, 1):
             x = dev16(torch, wl.activations(gx, M, K, "bf16"), torch.bfloat16)
@@ -338,7 +340,8 @@ def bench_small_single(torch, lb, reps=10, copies=64):
             nbytes = lb.packed_bytes("binary", N, K) + 2 * N * K // 128 + 2 * M * K + 2 * M * N
             gbs = nbytes / (us * 1e-6) / 1e9
             out[f"binary_{N}x{K}_M{M}"] = dict(us_per_launch=round(us, 2), bytes_per_launch=nbytes,
-                                               GBps=round(gbs, 1), frac_hbm_peak=round(gbs / PEAK_HBM_GBS, 4))
+                                               GBps=round(gbs, 1), frac_hbm_peak=round(gbs / PEAK_HBM_GBS, 4),
+                                               weight_copies=copies)
             del graph, x, y, ws
         del ws_, p0, s0
         torch.cuda.empty_cache()
