@@ -275,6 +275,48 @@ def bench_large_sweep(torch, lb, passes=3):
                 tflops=round(tf, 1), frac_mfma_peak=round(tf / PEAK_BF16_TFLOPS, 4))
 
 
+def bench_m1536(torch, lb, reps=200):
+    """Context: the 512x512 step's token count (M = 1536) on the linears of the
+    workloads quoted there: ternary 3072 x 3072 with bias (bf16), binary
+    3072 x 3072 and the binary fused QKV 9216 x 3072, each beside torch.matmul
+    (hipBLASLt) with dense bf16 weights of the same shape."""
+    import workloads as wl
+    out = {}
+    for name, fmt, N, K, bias in (("ternary_3072x3072_bias", "ternary", 3072, 3072, True),
+                                  ("binary_3072x3072", "binary", 3072, 3072, False),
+                                  ("binary_9216x3072", "binary", 9216, 3072, False)):
+        lin = wl.make_linear(name, fmt, 1536, N, K, seed=13, with_bias=bias)
+        c = torch.from_numpy(lin.codes).cuda()
+        p = lb.pack_ternary(c) if fmt == "ternary" else lb.pack_binary(c)
+        del c
+        sc = dev16(torch, lin.scales, torch.float16)
+        x = dev16(torch, lin.x, torch.bfloat16)
+        b = dev16(torch, lin.bias, torch.float16) if bias else None
+        y = torch.empty((1536, N), dtype=torch.bfloat16, device="cuda")
+        wd = torch.randn((K, N), generator=torch.Generator(device="cuda").manual_seed(14), device="cuda").bfloat16()
+
+        def timed(fn):
+            for _ in range(50):
+                fn()
+            torch.cuda.synchronize()
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            t0.record()
+            for _ in range(reps):
+                fn()
+            t1.record()
+            torch.cuda.synchronize()
+            return t0.elapsed_time(t1) / reps
+        ms = timed(lambda: lb.gemm(x, p, sc, fmt, bias=b, out=y))
+        msd = timed(lambda: torch.matmul(x, wd))
+        flop = 2.0 * 1536 * N * K
+        out[name] = dict(us=round(ms * 1e3, 1), tflops=round(flop / (ms * 1e-3) / 1e12, 1),
+                         dense_bf16_us=round(msd * 1e3, 1), dense_bf16_tflops=round(flop / (msd * 1e-3) / 1e12, 1))
+        del p, sc, x, b, y, wd
+    torch.cuda.empty_cache()
+    return out
+
+
 def hbm_copy(torch, nbytes=1 << 30, reps=10):
     """Context: a device-to-device copy of 1 GiB (reads and writes counted)."""
     src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
@@ -608,8 +650,9 @@ def main():
     ap.add_argument("--no-small", action="store_true")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the context runs that launch the same kernels as the timed paths "
-                         "(the 100-linear pass at M = 4608, the single binary linears) and the "
-                         "device copy, so that kernel traces and counters cover the timed paths only")
+                         "(the 100-linear pass at M = 4608, the M = 1536 linears, the single binary "
+                         "linears) and the device copy, so that kernel traces and counters cover the "
+                         "timed paths only")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run the counter-calibration workload instead of the benchmark")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -656,6 +699,7 @@ def main():
     dense = bench_dense(torch, r["M"], r["N1"], r["K1"], r["N2"])
     sweep = None if args.no_context else bench_large_sweep(torch, lb)
     copy = None if args.no_context else hbm_copy(torch)
+    m1536 = None if args.no_context else bench_m1536(torch, lb)
     small = None if args.no_small else bench_small(torch, lb)
     small_fused = None if args.no_small else bench_small(torch, lb, fuse_qkv=True)
     small_grouped = None if args.no_small else bench_small(torch, lb, fuse_qkv=True, grouped=True)
@@ -698,6 +742,7 @@ def main():
         "dense_bf16_matmul": dense,
         "large_m_sweep": sweep,
         "hbm_copy": copy,
+        "m1536": m1536,
         "small_m": small,
         "small_m_fused_qkv": small_fused,
         "small_m_grouped": small_grouped,
