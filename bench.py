@@ -588,6 +588,82 @@ def stats_table(stats_csv: str, limit: int = 24) -> str:
     return "\n".join(out)
 
 
+def cpu_configs(torch, lb):
+    """The oracle (float64 NumPy, all host cores) per workload configuration,
+    its dequantisation and its matrix product timed separately, beside the
+    GPU time of the same call (HIP events, inputs resident): the 64 x 256 x 256
+    case, the 1536-token ternary linear with bias, the MLP pair of the
+    1024 x 1024 step, the binary linears at M = 1536, 16 and 1, and one pass
+    of the 100 linears at M = 4608, whose oracle runs on a seeded sample of
+    256 rows per linear and is scaled to 4608 rows (an extrapolation)."""
+    import oracle
+    import workloads as wl
+
+    def gpu_ms(lin, x_bits=None, reps=20):
+        xb = lin.x if x_bits is None else x_bits
+        x = dev16(torch, xb, torch.bfloat16 if lin.x_dtype == "bf16" else torch.float16)
+        c = torch.from_numpy(lin.codes).cuda()
+        p = lb.pack_ternary(c) if lin.fmt == "ternary" else lb.pack_binary(c)
+        del c
+        sc = dev16(torch, lin.scales, torch.float16)
+        b = dev16(torch, lin.bias, torch.float16) if lin.bias is not None else None
+        for _ in range(5):
+            lb.gemm(x, p, sc, lin.fmt, bias=b)
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            lb.gemm(x, p, sc, lin.fmt, bias=b)
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / reps
+
+    def oracle_s(lin, rows=None):
+        xb = lin.x if rows is None else lin.x[rows]
+        t0 = time.perf_counter()
+        W = oracle.dequantize(lin.codes, lin.scales)
+        t1 = time.perf_counter()
+        A = oracle.decode(xb, lin.x_dtype) @ W.T
+        if lin.bias is not None:
+            A = A + lin.bias.astype(np.float64)[None, :]
+        t2 = time.perf_counter()
+        return t1 - t0, t2 - t1
+
+    out = {"cores": len(os.sched_getaffinity(0))}
+    cases = [("64x256x256_ternary_f16", wl.config1()), ("1536x3072x3072_ternary_bias", wl.config2())]
+    up, down = wl.config3()
+    if down.x is None:       # its input is the up-projection's GELU; any bf16 of that shape times the same
+        down.x = wl.activations(wl.generator(78), down.M, down.K, "bf16")
+    cases += [("4608x9216x3072_mlp_up", up), ("4608x3072x9216_mlp_down", down)]
+    for M in (1536, 16, 1):
+        for lin in wl.config4(M):
+            cases.append((f"{M}x{lin.N}x{lin.K}_binary", lin))
+    for name, lin in cases:
+        print(f"[cpu-configs] {name}", file=sys.stderr, flush=True)
+        dq, mm = oracle_s(lin)
+        g = gpu_ms(lin)
+        out[name] = dict(oracle_dequant_s=round(dq, 4), oracle_matmul_s=round(mm, 4), gpu_ms=round(g, 4),
+                         speedup=round((dq + mm) / (g * 1e-3), 1))
+    # one pass of the 100 linears at M = 4608 (oracle on 256 rows per linear, scaled)
+    xs = wl.config5_activations()
+    rows = np.sort(wl.generator(77).choice(4608, size=256, replace=False))
+    dq = mm = g = 0.0
+    for i, (name, codes, scales) in enumerate(wl.config5_weights()):
+        if i % 10 == 0:
+            print(f"[cpu-configs] 100 linears: {i}", file=sys.stderr, flush=True)
+        N, K = codes.shape
+        lin = wl.Linear(name, "ternary", 4608, N, K, "bf16", "bf16", xs[K], codes, scales)
+        d, m = oracle_s(lin, rows)
+        dq += d
+        mm += m * 4608 / 256
+        g += gpu_ms(lin, reps=3)
+    out["100_linears_M4608"] = dict(oracle_dequant_s=round(dq, 2), oracle_matmul_s_extrapolated=round(mm, 1),
+                                    gpu_ms=round(g, 3), speedup=round((dq + mm) / (g * 1e-3), 1),
+                                    oracle_sample="256 of 4608 rows per linear, matmul time x 18")
+    return out
+
+
 def dispatch_table(trace_csv: str, kernel: str) -> str:
     """Markdown table of the dispatches of one kernel in a rocprofv3
     --kernel-trace kernel_trace.csv, grouped by grid size (threads)."""
@@ -657,6 +733,9 @@ def main():
                     help="run the counter-calibration workload instead of the benchmark")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM traffic summary from the two counter runs and exit")
+    ap.add_argument("--cpu-configs", action="store_true",
+                    help="time the oracle per workload configuration beside the GPU (about two minutes "
+                         "of host work) and print that JSON instead of the benchmark line")
     ap.add_argument("--dispatch-table", nargs=2, metavar=("TRACE_CSV", "KERNEL"),
                     help="print one kernel's dispatches from a rocprofv3 kernel_trace.csv by grid size")
     ap.add_argument("--stats-table", metavar="STATS_CSV",
@@ -689,6 +768,9 @@ def main():
     lb.lib()
     if args.traffic_probe:
         traffic_probe(torch, lb)
+        return
+    if args.cpu_configs:
+        print(json.dumps(cpu_configs(torch, lb)), flush=True)
         return
 
     r = bench_large(torch, lb, args.steps, args.warmup)
