@@ -142,3 +142,15 @@ def test_argument_errors_before_any_device_work(L):
     assert L.lowbit_gemm_grouped_workspace_bytes(0, b.TERNARY, 16, 64, 256) == 0
     assert L.lowbit_gemm_grouped_workspace_bytes(9, b.TERNARY, 16, 64, 256) == 0
     assert L.lowbit_gelu(P, P, b.NONE, 10, None) == b.ERR_DTYPE
+
+
+@pytest.mark.skipif(__import__("torch").cuda.device_count() > 0, reason="checks the no-GPU answer")
+def test_valid_call_without_a_gpu_reports_no_device(L):
+    """Every host check passes, then the device check answers LOWBIT_ERR_DEVICE."""
+    import bit_weight_gemm_int2_amd as b
+    P = 1 << 20
+    assert L.lowbit_init() == b.ERR_DEVICE
+    assert L.lowbit_gemm(b.TERNARY, P, b.BF16, 16, 256, 256, P, P, 128, 64, None, b.NONE,
+                         P, b.BF16, 64, 0, None, 0, None) == b.ERR_DEVICE
+    assert L.pack_ternary(P, 4, 16, P, None, None) == b.ERR_DEVICE
+    assert L.lowbit_gemm_workspace_bytes(b.TERNARY, 16, 3072, 9216) == 0

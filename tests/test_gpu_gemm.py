@@ -1,6 +1,7 @@
 """GPU GEMM parity against the CPU oracle, element by element, within the stated
 tolerance |d| <= 1e-3 * sum_k |x_k w_k| + 1e-5 (+ half an output ulp for
 16-bit outputs); bit-exact where every partial sum is exact in FP32."""
+import ctypes
 import os
 
 import numpy as np
@@ -392,6 +393,43 @@ def test_gelu_kernel(lb):
             lim = lim + 0.5 * oracle.ulp(np.maximum(abs(ref), abs(y)), dt)
         bad = np.flatnonzero(np.abs(y - ref) > lim)
         assert bad.size == 0, (dt, [(float(xin[i]), float(y[i]), float(ref[i]), float(lim[i])) for i in bad[:5]])
+
+
+def test_workspace_errors(lb, force_variant):
+    """A call whose plan needs a workspace: none, one byte too small, or not
+    256-byte aligned is refused before any launch (single and grouped)."""
+    force_variant("small-split")
+    M, N, K = 16, 3072, 9216
+    L = lb.lib()
+    need = L.lowbit_gemm_workspace_bytes(lb.TERNARY, M, N, K)
+    assert need > 0
+    x = torch.zeros((M, K), dtype=torch.bfloat16, device="cuda")
+    p = torch.zeros((N, K // 4), dtype=torch.uint8, device="cuda")
+    s = torch.zeros((N, K // 128), dtype=torch.float16, device="cuda")
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ws = torch.zeros(need + 512, dtype=torch.uint8, device="cuda")
+
+    def call(wptr, wbytes):
+        return L.lowbit_gemm(lb.TERNARY, x.data_ptr(), lb.BF16, M, K, K, p.data_ptr(), s.data_ptr(), 128, N,
+                             None, lb.NONE, y.data_ptr(), lb.BF16, N, 0, wptr, wbytes, None)
+    assert call(None, 0) == lb.ERR_WORKSPACE
+    assert call(ws.data_ptr(), need - 1) == lb.ERR_WORKSPACE
+    assert call(ws.data_ptr() + 16, need) == lb.ERR_ALIGN
+    assert call(ws.data_ptr(), need) == lb.OK
+    arr = lambda *ptrs: (ctypes.c_void_p * len(ptrs))(*ptrs)
+    gneed = L.lowbit_gemm_grouped_workspace_bytes(2, lb.TERNARY, M, N, K)
+    assert gneed > need
+
+    def gcall(wptr, wbytes):
+        return L.lowbit_gemm_grouped(2, lb.TERNARY, arr(x.data_ptr(), x.data_ptr()), lb.BF16, M, K, K,
+                                     arr(p.data_ptr(), p.data_ptr()), arr(s.data_ptr(), s.data_ptr()), 128, N,
+                                     None, lb.NONE, arr(y.data_ptr(), y.data_ptr()), lb.BF16, N, 0,
+                                     wptr, wbytes, None)
+    gws = torch.zeros(gneed, dtype=torch.uint8, device="cuda")
+    assert gcall(ws.data_ptr(), need) == lb.ERR_WORKSPACE
+    assert gcall(None, 0) == lb.ERR_WORKSPACE
+    torch.cuda.synchronize()
+    del gws
 
 
 def test_device_side_errors(lb):
