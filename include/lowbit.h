@@ -23,6 +23,13 @@
  *  - The library runs on gfx950 only; other devices get LOWBIT_ERR_DEVICE.
  *  - Every call is stateless apart from a per-device cache of device
  *    properties, and is safe to call from several host threads.
+ *  - Test hook: the environment variable LOWBIT_FORCE_VARIANT, read on every
+ *    call, forces one kernel family so that tests reach every launch path:
+ *    "large" (the large-M kernel at any M), "small" (the small-M kernels
+ *    only), "large-wide" / "large-pair" (one large-M tile configuration),
+ *    "small-split" (the small-M column-tile kernel with its K split across
+ *    workgroups). Results keep the same accuracy contract under every
+ *    variant, and the workspace queries follow it; leave it unset otherwise.
  *
  * Packed weight layout (this library's own; the pages fix only "2 bits per
  * ternary" and "1 bit per binary weight")
