@@ -154,3 +154,26 @@ def test_valid_call_without_a_gpu_reports_no_device(L):
                          P, b.BF16, 64, 0, None, 0, None) == b.ERR_DEVICE
     assert L.pack_ternary(P, 4, 16, P, None, None) == b.ERR_DEVICE
     assert L.lowbit_gemm_workspace_bytes(b.TERNARY, 16, 3072, 9216) == 0
+
+
+C_EXAMPLE = os.path.join(ROOT, "tests", "c", "abi_example.c")
+
+
+def build_c_example(out_dir):
+    """Compile the plain C user of the ABI with gcc against include/ and the
+    in-tree library; returns the executable's path."""
+    import bit_weight_gemm_int2_amd as b
+    exe = os.path.join(out_dir, "abi_example")
+    libdir = os.path.dirname(b.LIB_PATH)
+    cmd = ["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), "-o", exe, C_EXAMPLE,
+           "-L", libdir, "-llowbit", "-L/opt/rocm/lib", "-lamdhip64",
+           f"-Wl,-rpath,{libdir}", "-Wl,-rpath,/opt/rocm/lib"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    return exe
+
+
+def test_c_program_builds_against_the_header(L, tmp_path):
+    """The ABI is usable from C alone: a C99 program includes lowbit.h and
+    links liblowbit.so with gcc, no C++ and no Python."""
+    assert os.path.exists(build_c_example(str(tmp_path)))
