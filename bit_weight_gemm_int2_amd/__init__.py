@@ -19,7 +19,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblowbit.so")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_GROUP, ERR_WORKSPACE, ERR_DEVICE, ERR_HIP = range(9)
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_GROUP, ERR_WORKSPACE, ERR_DEVICE, ERR_HIP, ERR_OVERLAP = range(10)
 F16, BF16, F32, NONE = 0, 1, 2, 3
 BINARY, TERNARY, BASE3 = 1, 2, 3
 ACT_NONE, ACT_GELU = 0, 1

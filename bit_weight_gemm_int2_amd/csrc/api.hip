@@ -62,6 +62,13 @@ int32_t current_device(int* num_cu) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// [p, p + bytes) and [q, q + qbytes) share a byte (empty ranges never do)
+bool overlaps(const void* p, int64_t bytes, const void* q, int64_t qbytes) {
+  if (!p || !q || bytes <= 0 || qbytes <= 0) return false;
+  const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+  return a < b + (uintptr_t)qbytes && b < a + (uintptr_t)bytes;
+}
+
 int force_variant() {
   const char* v = std::getenv("LOWBIT_FORCE_VARIANT");
   if (!v) return 0;
@@ -95,6 +102,7 @@ const char* lowbit_status_string(int32_t s) {
     case LOWBIT_ERR_WORKSPACE: return "workspace missing or too small";
     case LOWBIT_ERR_DEVICE: return "current device is not a gfx950 GPU";
     case LOWBIT_ERR_HIP: return "HIP runtime error";
+    case LOWBIT_ERR_OVERLAP: return "an output overlaps an input or another output";
     default: return "unknown status";
   }
 }
@@ -126,6 +134,10 @@ static int32_t pack_common(int fmt, const int8_t* codes, int64_t N, int64_t K, u
   if (lowbit_packed_bytes(fmt, N, K) < 0) return LOWBIT_ERR_SHAPE;
   if (!aligned(codes, 16) || !aligned(packed, 16) || (invalid_count && !aligned(invalid_count, 4)))
     return LOWBIT_ERR_ALIGN;
+  const int64_t pbytes = lowbit_packed_bytes(fmt, N, K);
+  if (overlaps(packed, pbytes, codes, N * K) || overlaps(invalid_count, 4, codes, N * K) ||
+      overlaps(invalid_count, 4, packed, pbytes))
+    return LOWBIT_ERR_OVERLAP;
   int32_t st = current_device(nullptr);
   if (st) return st;
   hipError_t e = lowbit::launch_pack(kernel_format(fmt), codes, N, K, packed, invalid_count,
@@ -156,6 +168,10 @@ int32_t unpack_lowbit(int32_t format, const uint8_t* packed, int64_t N, int64_t 
   if (lowbit_packed_bytes(format, N, K) < 0) return LOWBIT_ERR_SHAPE;
   if (!aligned(codes, 16) || !aligned(packed, 16) || (invalid_count && !aligned(invalid_count, 4)))
     return LOWBIT_ERR_ALIGN;
+  const int64_t pbytes = lowbit_packed_bytes(format, N, K);
+  if (overlaps(codes, N * K, packed, pbytes) || overlaps(invalid_count, 4, codes, N * K) ||
+      overlaps(invalid_count, 4, packed, pbytes))
+    return LOWBIT_ERR_OVERLAP;
   int32_t st = current_device(nullptr);
   if (st) return st;
   hipError_t e = lowbit::launch_unpack(kernel_format(format), packed, N, K, codes, invalid_count,
@@ -169,6 +185,9 @@ int32_t base3_to_int2(const uint8_t* base3, int64_t N, int64_t K, uint8_t* int2,
   if (lowbit_packed_bytes(LOWBIT_TERNARY_INT2, N, K) < 0) return LOWBIT_ERR_SHAPE;
   if (!aligned(base3, 16) || !aligned(int2, 16) || (invalid_count && !aligned(invalid_count, 4)))
     return LOWBIT_ERR_ALIGN;
+  const int64_t b3 = lowbit_packed_bytes(LOWBIT_TERNARY_BASE3, N, K), i2 = N * (K / 4);
+  if (overlaps(int2, i2, base3, b3) || overlaps(invalid_count, 4, base3, b3) || overlaps(invalid_count, 4, int2, i2))
+    return LOWBIT_ERR_OVERLAP;
   int32_t st = current_device(nullptr);
   if (st) return st;
   hipError_t e = lowbit::launch_base3_to_int2(base3, N, K, int2, invalid_count, (hipStream_t)stream);
@@ -222,7 +241,17 @@ int32_t check_problem(int32_t format, const void* X, int32_t x_dtype, int64_t M,
   if (!aligned(X, 16) || !aligned(W_packed, 16) || !aligned(scales, 2) || !aligned(Y, ysz) || ldx % 8)
     return LOWBIT_ERR_ALIGN;
   if (bias && !aligned(bias, bias_dtype == LOWBIT_F32 ? 4 : 2)) return LOWBIT_ERR_ALIGN;
+  const int64_t yb = ((M - 1) * ldy + N) * (int64_t)ysz;
+  if (overlaps(Y, yb, X, ((M - 1) * ldx + K) * 2) || overlaps(Y, yb, W_packed, N * wrow) ||
+      overlaps(Y, yb, scales, N * (K / 128) * 2) ||
+      overlaps(Y, yb, bias, N * (bias_dtype == LOWBIT_F32 ? 4 : 2)))
+    return LOWBIT_ERR_OVERLAP;
   return LOWBIT_OK;
+}
+
+// bytes of Y one problem addresses
+int64_t y_span(int64_t M, int64_t N, int64_t ldy, int32_t y_dtype) {
+  return ((M - 1) * ldy + N) * (y_dtype == LOWBIT_F32 ? 4 : 2);
 }
 
 lowbit::GemmArgs make_args(int32_t format, int64_t K, int64_t ldx, const uint8_t* W_packed, const void* scales,
@@ -281,6 +310,9 @@ int32_t lowbit_gemm(int32_t format, const void* X, int32_t x_dtype, int64_t M, i
   size_t need = lowbit_gemm_workspace_bytes(format, M, N, K);
   if (need && (!workspace || workspace_bytes < need)) return LOWBIT_ERR_WORKSPACE;
   if (need && !aligned(workspace, 256)) return LOWBIT_ERR_ALIGN;
+  if (need && (overlaps(workspace, (int64_t)need, Y, y_span(M, N, ldy, y_dtype)) ||
+               overlaps(workspace, (int64_t)need, X, ((M - 1) * ldx + K) * 2)))
+    return LOWBIT_ERR_OVERLAP;
   const lowbit::GemmArgs a = make_args(format, K, ldx, W_packed, scales, N, bias, bias_dtype, y_dtype, ldy,
                                        activation, workspace);
   return run_problem(format, X, x_dtype, M, K, ldx, a, Y, y_dtype, ldy, rows_max, num_cu, force_variant(), stream);
@@ -315,6 +347,17 @@ int32_t lowbit_gemm_grouped(int32_t count, int32_t format, const void* const* X,
                                bias ? bias[z] : nullptr, bias_dtype, Y[z], y_dtype, ldy, activation, &rows_max);
     if (st) return st;
   }
+  // each output against every other problem's inputs and output
+  const int64_t yb = y_span(M, N, ldy, y_dtype);
+  const int64_t wrow = format == LOWBIT_TERNARY_INT2 ? K / 4 : K / 8;
+  for (int z = 0; z < count; ++z)
+    for (int u = 0; u < count; ++u) {
+      if (u == z) continue;
+      if (overlaps(Y[z], yb, Y[u], yb) || overlaps(Y[z], yb, X[u], ((M - 1) * ldx + K) * 2) ||
+          overlaps(Y[z], yb, W_packed[u], N * wrow) || overlaps(Y[z], yb, scales[u], N * (K / 128) * 2) ||
+          (bias && overlaps(Y[z], yb, bias[u], N * (bias_dtype == LOWBIT_F32 ? 4 : 2))))
+        return LOWBIT_ERR_OVERLAP;
+    }
   int num_cu = 0;
   int32_t st = current_device(&num_cu);
   if (st) return st;
@@ -357,6 +400,8 @@ int32_t lowbit_gelu(const void* in, void* out, int32_t dtype, int64_t count, voi
   if (dtype != LOWBIT_F16 && dtype != LOWBIT_BF16 && dtype != LOWBIT_F32) return LOWBIT_ERR_DTYPE;
   if (count < 1) return LOWBIT_ERR_SHAPE;
   if (!aligned(in, 16) || !aligned(out, 16)) return LOWBIT_ERR_ALIGN;
+  const int64_t bytes = count * (dtype == LOWBIT_F32 ? 4 : 2);
+  if (in != out && overlaps(in, bytes, out, bytes)) return LOWBIT_ERR_OVERLAP;
   int32_t st = current_device(nullptr);
   if (st) return st;
   hipError_t e = lowbit::launch_gelu(in, out, dtype, count, (hipStream_t)stream);

@@ -16,7 +16,11 @@
  *    never allocates, frees or synchronises; work is enqueued on `stream`
  *    (a hipStream_t; NULL means the null stream) and runs asynchronously.
  *  - The return value reports argument errors (checked on the host before any
- *    launch) and launch errors (hipGetLastError after the launch). Errors
+ *    launch) and launch errors (hipGetLastError after the launch).
+ *  - Outputs may not overlap inputs (or, for lowbit_gemm_grouped, each other):
+ *    the byte ranges each call addresses are compared on the host and an
+ *    overlap returns LOWBIT_ERR_OVERLAP (lowbit_gelu alone may run in place,
+ *    with in == out exactly). Errors
  *    that happen later on the device surface at the caller's next
  *    synchronisation, as for any HIP kernel.
  *  - Matrices are row-major. Sizes are element counts unless stated.
@@ -79,7 +83,8 @@ typedef enum {
   LOWBIT_ERR_GROUP = 5,      /* group size other than 128                       */
   LOWBIT_ERR_WORKSPACE = 6,  /* workspace missing or smaller than required      */
   LOWBIT_ERR_DEVICE = 7,     /* current device is not gfx950, or no device      */
-  LOWBIT_ERR_HIP = 8         /* the HIP runtime reported an error               */
+  LOWBIT_ERR_HIP = 8,        /* the HIP runtime reported an error               */
+  LOWBIT_ERR_OVERLAP = 9     /* an output's bytes overlap an input's or another output's */
 } lowbit_status;
 
 typedef enum { LOWBIT_F16 = 0, LOWBIT_BF16 = 1, LOWBIT_F32 = 2, LOWBIT_NONE = 3 } lowbit_dtype;

@@ -63,7 +63,7 @@ def test_host_only_queries(L):
     assert L.lowbit_packed_bytes(b.BASE3, 1, 1 << 31) == -1
     assert L.lowbit_scale_count(3072, 9216, 128) == 3072 * 72
     assert L.lowbit_scale_count(3072, 9216, 64) == -1
-    for s in range(9):
+    for s in range(10):
         assert len(L.lowbit_status_string(s)) > 0
     assert L.lowbit_status_string(99) == b"unknown status"
 
@@ -71,9 +71,10 @@ def test_host_only_queries(L):
 def test_argument_errors_before_any_device_work(L):
     """Every status that the host check returns before touching the device."""
     import bit_weight_gemm_int2_amd as b
-    P = 1 << 20            # fake, 16-byte-aligned non-NULL "device" address
-    good = dict(fmt=b.TERNARY, X=P, xd=b.BF16, M=16, K=256, ldx=256, W=P, S=P, group=128, N=64,
-                bias=None, bd=b.NONE, Y=P, yd=b.BF16, ldy=64, act=0, ws=None, wsb=0)
+    P = 1 << 20            # fake, 16-byte-aligned non-NULL "device" addresses, far apart
+    PX, PW, PS, PY, PB = (k << 36 for k in range(1, 6))
+    good = dict(fmt=b.TERNARY, X=PX, xd=b.BF16, M=16, K=256, ldx=256, W=PW, S=PS, group=128, N=64,
+                bias=None, bd=b.NONE, Y=PY, yd=b.BF16, ldy=64, act=0, ws=None, wsb=0)
 
     def call(**kw):
         a = dict(good, **kw)
@@ -125,10 +126,10 @@ def test_argument_errors_before_any_device_work(L):
     arr = lambda *ptrs: (ctypes.c_void_p * len(ptrs))(*ptrs)
 
     def grouped(count=2, X=None, W=None, S=None, Y=None, bias=None, bd=b.NONE, fmt=b.TERNARY, M=16):
-        X = arr(P, P) if X is None else X
-        W = arr(P, P) if W is None else W
-        S = arr(P, P) if S is None else S
-        Y = arr(P, P) if Y is None else Y
+        X = arr(PX, PX) if X is None else X           # inputs may be shared
+        W = arr(PW, PW) if W is None else W
+        S = arr(PS, PS) if S is None else S
+        Y = arr(PY, PY + (1 << 30)) if Y is None else Y
         return L.lowbit_gemm_grouped(count, fmt, X, b.BF16, M, 256, 256, W, S, 128, 64, bias, bd,
                                      Y, b.BF16, 64, 0, None, 0, None)
     assert grouped(count=0) == b.ERR_SHAPE
@@ -139,6 +140,21 @@ def test_argument_errors_before_any_device_work(L):
     assert grouped(bd=b.F16) == b.ERR_NULL                       # bias dtype without biases
     assert L.lowbit_gemm_grouped(2, b.TERNARY, None, b.BF16, 16, 256, 256, arr(P, P), arr(P, P), 128, 64,
                                  None, b.NONE, arr(P, P), b.BF16, 64, 0, None, 0, None) == b.ERR_NULL
+    assert grouped(Y=arr(PY, PY + 64)) == b.ERR_OVERLAP            # two outputs share bytes
+    assert grouped(Y=arr(PY, PX)) == b.ERR_OVERLAP                 # an output on an input
+    # outputs overlapping inputs, everywhere
+    assert call(Y=PX) == b.ERR_OVERLAP
+    assert call(Y=PX + 256 * 2 * 15) == b.ERR_OVERLAP             # into X's last row
+    assert call(Y=PW + 1024) == b.ERR_OVERLAP
+    assert call(Y=PS) == b.ERR_OVERLAP
+    assert call(bias=PY + 64, bd=b.F16) == b.ERR_OVERLAP
+    assert L.pack_ternary(PX, 4, 16, PX + 32, None, None) == b.ERR_OVERLAP
+    assert L.pack_base3(PX, 4, 16, PX + 48, None, None) == b.ERR_OVERLAP
+    assert L.unpack_lowbit(b.TERNARY, PX, 4, 16, PX, None, None) == b.ERR_OVERLAP
+    assert L.base3_to_int2(PX, 4, 16, PX, None, None) == b.ERR_OVERLAP
+    assert L.pack_ternary(PX, 4, 16, PW, PX + 2, None) == b.ERR_ALIGN    # counter checked for alignment first
+    assert L.pack_ternary(PX, 4, 16, PW, PX + 16, None) == b.ERR_OVERLAP  # then for overlap
+    assert L.lowbit_gelu(PX, PX + 16, b.BF16, 100, None) == b.ERR_OVERLAP
     assert L.lowbit_gemm_grouped_workspace_bytes(0, b.TERNARY, 16, 64, 256) == 0
     assert L.lowbit_gemm_grouped_workspace_bytes(9, b.TERNARY, 16, 64, 256) == 0
     assert L.lowbit_gelu(P, P, b.NONE, 10, None) == b.ERR_DTYPE
@@ -148,11 +164,12 @@ def test_argument_errors_before_any_device_work(L):
 def test_valid_call_without_a_gpu_reports_no_device(L):
     """Every host check passes, then the device check answers LOWBIT_ERR_DEVICE."""
     import bit_weight_gemm_int2_amd as b
-    P = 1 << 20
+    PX, PW, PS, PY = (k << 36 for k in range(1, 5))
     assert L.lowbit_init() == b.ERR_DEVICE
-    assert L.lowbit_gemm(b.TERNARY, P, b.BF16, 16, 256, 256, P, P, 128, 64, None, b.NONE,
-                         P, b.BF16, 64, 0, None, 0, None) == b.ERR_DEVICE
-    assert L.pack_ternary(P, 4, 16, P, None, None) == b.ERR_DEVICE
+    assert L.lowbit_gemm(b.TERNARY, PX, b.BF16, 16, 256, 256, PW, PS, 128, 64, None, b.NONE,
+                         PY, b.BF16, 64, 0, None, 0, None) == b.ERR_DEVICE
+    assert L.pack_ternary(PX, 4, 16, PW, None, None) == b.ERR_DEVICE
+    assert L.lowbit_gelu(PX, PX, b.BF16, 100, None) == b.ERR_DEVICE     # in place is allowed
     assert L.lowbit_gemm_workspace_bytes(b.TERNARY, 16, 3072, 9216) == 0
 
 

@@ -407,6 +407,7 @@ def test_workspace_errors(lb, force_variant):
     p = torch.zeros((N, K // 4), dtype=torch.uint8, device="cuda")
     s = torch.zeros((N, K // 128), dtype=torch.float16, device="cuda")
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    y2 = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     ws = torch.zeros(need + 512, dtype=torch.uint8, device="cuda")
 
     def call(wptr, wbytes):
@@ -423,7 +424,7 @@ def test_workspace_errors(lb, force_variant):
     def gcall(wptr, wbytes):
         return L.lowbit_gemm_grouped(2, lb.TERNARY, arr(x.data_ptr(), x.data_ptr()), lb.BF16, M, K, K,
                                      arr(p.data_ptr(), p.data_ptr()), arr(s.data_ptr(), s.data_ptr()), 128, N,
-                                     None, lb.NONE, arr(y.data_ptr(), y.data_ptr()), lb.BF16, N, 0,
+                                     None, lb.NONE, arr(y.data_ptr(), y2.data_ptr()), lb.BF16, N, 0,
                                      wptr, wbytes, None)
     gws = torch.zeros(gneed, dtype=torch.uint8, device="cuda")
     assert gcall(ws.data_ptr(), need) == lb.ERR_WORKSPACE
