@@ -184,11 +184,21 @@ def base3_to_int2(packed: torch.Tensor, K: int, check: bool = True, out: Optiona
     return _counted(lib().base3_to_int2, packed, N, K, out, check, stream, "invalid base-3 value(s)")
 
 
+def _check_packed(fmt, packed: torch.Tensor, N: int, K: int):
+    """The library reads N x (bytes per row) packed bytes: check the tensor holds them."""
+    if packed.dtype != torch.uint8 or packed.dim() != 2:
+        raise ValueError("packed must be a 2-D uint8 tensor")
+    row = _row_bytes(_FMT[fmt], K)
+    if tuple(packed.shape) != (N, row):
+        raise ValueError(f"packed must be [{N}, {row}] for K = {K}, got {list(packed.shape)}")
+
+
 def unpack(fmt, packed: torch.Tensor, K: int, stream=None) -> Tuple[torch.Tensor, int]:
     """packed [N, K/4, K/8 or ceil(K/5)] -> (int8 codes [N, K], number of invalid codes)."""
     _cuda(packed, "packed")
     packed = packed.contiguous()
     N = packed.shape[0]
+    _check_packed(fmt, packed, N, K)
     codes = torch.empty((N, K), dtype=torch.int8, device=packed.device)
     cnt = torch.empty(1, dtype=torch.int32, device=packed.device)
     _check(lib().unpack_lowbit(_FMT[fmt], packed.data_ptr(), N, K, codes.data_ptr(), cnt.data_ptr(),
@@ -212,11 +222,21 @@ def gemm(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, fmt, bias:
     N = packed.shape[0]
     packed = packed.contiguous()
     scales = scales.contiguous()
-    if scales.dtype != torch.float16:
-        raise ValueError("scales must be float16")
+    if x.dtype not in (torch.float16, torch.bfloat16):
+        raise ValueError("x must be float16 or bfloat16")
+    _check_packed(fmt, packed, N, K)
+    if scales.dtype != torch.float16 or tuple(scales.shape) != (N, K // GROUP):
+        raise ValueError(f"scales must be float16 [{N}, {K // GROUP}]")
+    if bias is not None:
+        _cuda(bias, "bias")
+        bias = bias.contiguous()
+        if bias.numel() != N or bias.dtype not in _DT:
+            raise ValueError(f"bias must hold {N} float16, bfloat16 or float32 values")
     odt = out_dtype or x.dtype
     if out is None:
         out = torch.empty((M, N), dtype=odt, device=x.device)
+    elif tuple(out.shape) != (M, N) or out.dim() != 2 or out.stride(1) != 1 or out.dtype not in _DT:
+        raise ValueError(f"out must be [{M}, {N}] with unit stride along N")
     ws_need = workspace_bytes(fmt, M, N, K)
     if ws_need and workspace is None:
         workspace = _shared_workspace(x.device, ws_need)
@@ -260,14 +280,21 @@ def gemm_grouped(xs, packeds, scales, fmt, biases=None, out_dtype: Optional[torc
     packeds = [p.contiguous() for p in packeds]
     scales = [s_.contiguous() for s_ in scales]
     N = packeds[0].shape[0]
-    if any(p.shape != packeds[0].shape for p in packeds) or any(s_.dtype != torch.float16 for s_ in scales):
-        raise ValueError("packed weights of one shape and float16 scales")
+    for p in packeds:
+        _check_packed(fmt, p, N, K)
+    if any(s_.dtype != torch.float16 or tuple(s_.shape) != (N, K // GROUP) for s_ in scales):
+        raise ValueError(f"scales must be float16 [{N}, {K // GROUP}]")
     odt = out_dtype or x0.dtype
     if outs is None:
         outs = [torch.empty((M, N), dtype=odt, device=x0.device) for _ in range(count)]
+    elif len(outs) != count or any(tuple(y.shape) != (M, N) or y.stride(1) != 1 or y.dtype != outs[0].dtype
+                                   or y.stride(0) != outs[0].stride(0) for y in outs):
+        raise ValueError(f"outs: {count} tensors [{M}, {N}] of one dtype and row stride")
     bdt = NONE
     if biases is not None:
         biases = [b.contiguous() for b in biases]
+        if any(b.numel() != N or b.dtype != biases[0].dtype for b in biases):
+            raise ValueError(f"biases: {count} tensors of {N} values and one dtype")
         bdt = _DT[biases[0].dtype]
     need = int(lib().lowbit_gemm_grouped_workspace_bytes(count, _FMT[fmt], M, N, K))
     if need and workspace is None:

@@ -444,3 +444,32 @@ def test_device_side_errors(lb):
                        None, lb.NONE, y.data_ptr(), lb.BF16, 8, 0, None, 0, None)
     assert st == lb.OK if need == 0 else st == lb.ERR_WORKSPACE
     assert L.lowbit_init() == lb.OK
+
+
+def test_binding_refuses_mismatched_tensors(lb):
+    """The C ABI takes raw pointers and cannot see buffer sizes; the binding
+    checks every tensor against the problem's shape before the call."""
+    M, N, K = 8, 64, 256
+    x = torch.zeros((M, K), dtype=torch.bfloat16, device="cuda")
+    p = torch.zeros((N, K // 4), dtype=torch.uint8, device="cuda")
+    s = torch.zeros((N, K // 128), dtype=torch.float16, device="cuda")
+    with pytest.raises(ValueError, match="packed"):
+        lb.gemm(x, p[:, :32], s, "ternary")                       # codes for K = 128
+    with pytest.raises(ValueError, match="packed"):
+        lb.gemm(x, p, s, "binary")                                # ternary bytes as binary
+    with pytest.raises(ValueError, match="scales"):
+        lb.gemm(x, p, s[:, :1], "ternary")
+    with pytest.raises(ValueError, match="bias"):
+        lb.gemm(x, p, s, "ternary", bias=torch.zeros(N - 1, dtype=torch.float16, device="cuda"))
+    with pytest.raises(ValueError, match="out"):
+        lb.gemm(x, p, s, "ternary", out=torch.empty((M, N - 1), dtype=torch.bfloat16, device="cuda"))
+    with pytest.raises(ValueError, match="x must"):
+        lb.gemm(x.float(), p, s, "ternary")
+    with pytest.raises(ValueError, match="packed"):
+        lb.unpack("ternary", p, K + 16)
+    with pytest.raises(ValueError, match="scales"):
+        lb.gemm_grouped([x, x], [p, p], [s, s[:, :1]], "ternary")
+    with pytest.raises(ValueError, match="outs"):
+        lb.gemm_grouped([x, x], [p, p], [s, s], "ternary",
+                        outs=[torch.empty((M, N), dtype=torch.bfloat16, device="cuda")] * 1)
+    torch.cuda.synchronize()
