@@ -76,7 +76,7 @@ namespace lowbit {
 // ===========================================================================
 namespace large {
 // WN waves side by side along N: a tile is BMT x 64 WN (BMT = 128 by default)
-constexpr int BM = 128, STAGES = 3;
+constexpr int BM = 128;
 constexpr int ROW_BYTES = 256;                 // 128 k x 2 bytes
 template <int BMT> constexpr int x_bytes() { return BMT * ROW_BYTES; }   // activations per stage
 template <int WN> constexpr int bn() { return 64 * WN; }
