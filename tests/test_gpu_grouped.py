@@ -146,3 +146,21 @@ def test_grouped_graph_replay(lb):
         torch.cuda.synchronize()
         for z in range(count):
             assert torch.equal(ys[z].view(torch.int16), refs[z].view(torch.int16)), f"replay {r} problem {z}"
+
+
+@pytest.mark.parametrize("variant", ["large", "large-pair", "small", "small-split"])
+def test_grouped_under_forced_variants(lb, variant):
+    """Every kernel family a group can land on: forced large-M kernels run the
+    problems one launch each even at M <= 16; forced small-M kernels group them."""
+    banner(f"grouped forced {variant}")
+    old = os.environ.get("LOWBIT_FORCE_VARIANT")
+    os.environ["LOWBIT_FORCE_VARIANT"] = variant
+    try:
+        lins = _problems(3, "binary", 16, 1000, 4608, seed=7500)
+        Ys, _ = _run(lb, lins)
+        _check(lins, Ys, "bf16")
+    finally:
+        if old is None:
+            os.environ.pop("LOWBIT_FORCE_VARIANT", None)
+        else:
+            os.environ["LOWBIT_FORCE_VARIANT"] = old
