@@ -473,3 +473,34 @@ def test_binding_refuses_mismatched_tensors(lb):
         lb.gemm_grouped([x, x], [p, p], [s, s], "ternary",
                         outs=[torch.empty((M, N), dtype=torch.bfloat16, device="cuda")] * 1)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("bias_dtype", ["f16", "bf16", "f32"])
+@pytest.mark.parametrize("variant,M,N,K", [(None, 5, 520, 2048), ("small-split", 16, 3072, 9216),
+                                           ("large-pair", 200, 1030, 1152), ("large-wide", 130, 2100, 384)])
+def test_bias_dtypes_on_every_path(lb, force_variant, bias_dtype, variant, M, N, K):
+    """Bias in f16, bf16 or f32 is added once, in FP32, before the single
+    rounding: against the oracle's sum plus the bias's exact value."""
+    force_variant(variant)
+    lin = wl.make_linear("biasdt", "ternary", M, N, K, seed=880 + M, p0=0.35, with_bias=True)
+    b16 = lin.bias.astype(np.float32)
+    if bias_dtype == "f16":
+        bdev = torch.from_numpy(lin.bias.view(np.int16)).cuda().view(torch.float16)
+        bval = b16.astype(np.float64)
+    elif bias_dtype == "bf16":
+        bits = oracle.encode(b16.astype(np.float64) * 3.0, "bf16")     # values f16 cannot hold exactly
+        bdev = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+        bval = oracle.decode(bits, "bf16")
+    else:
+        v = (b16 * np.float32(1.0 / 3.0)).astype(np.float32)          # full FP32 significands
+        bdev = torch.from_numpy(v).cuda()
+        bval = v.astype(np.float64)
+    x = dev_bits(lin.x, "bf16")
+    packed, s = dev_weights("ternary", lin.codes, lin.scales)
+    y = lb.gemm(x, packed, s, "ternary", bias=bdev, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    A0 = oracle.linear(lin.x, "bf16", lin.codes, lin.scales)
+    Mg0 = oracle.magnitude(lin.x, "bf16", lin.codes, lin.scales)
+    A = A0 + bval[None, :]
+    Mg = Mg0 + np.abs(bval)[None, :]
+    _assert_parity(to_host64(y), A, Mg, "f32", f"bias {bias_dtype} {variant}")
