@@ -504,3 +504,55 @@ def test_bias_dtypes_on_every_path(lb, force_variant, bias_dtype, variant, M, N,
     A = A0 + bval[None, :]
     Mg = Mg0 + np.abs(bval)[None, :]
     _assert_parity(to_host64(y), A, Mg, "f32", f"bias {bias_dtype} {variant}")
+
+
+@pytest.mark.parametrize("variant,M", [(None, 4), ("small-split", 16), (None, 1), ("large-pair", 40),
+                                       ("large-wide", 40)])
+def test_special_scales_on_every_path(lb, force_variant, variant, M):
+    """Zero, subnormal, negative and large FP16 scales, through the small-M
+    kernels as well as the large-M ones."""
+    force_variant(variant)
+    g = wl.generator(410 + M)
+    N, K = 300, 2304
+    xb = wl.activations(g, M, K, "bf16")
+    t = wl.ternary_codes(g, N, K, 0.35)
+    s = wl.group_scales(g, N, K)
+    s[0, :] = 0
+    s[1, 1] = 0
+    s[2, :] = np.float16(2.0 ** -24)
+    s[3, 0] = np.float16(3.0 * 2.0 ** -20)
+    s[4, :] = -s[4, :]
+    s[5, 2] = np.float16(60000.0)
+    s[6, ::2] = 0
+    lin = wl.Linear("special2", "ternary", M, N, K, "bf16", "f32", xb, t, s, None)
+    Y, _ = run_linear(lin)
+    A, Mg = oracle_linear(lin)
+    _assert_parity(Y, A, Mg, "f32", f"special scales {variant}")
+    assert np.all(Y[:, 0] == 0.0)
+
+
+@pytest.mark.parametrize("variant,M", [(None, 4), ("small-split", 16), ("large-pair", 40), ("large-wide", 40)])
+def test_fp16_output_overflows_to_infinity(lb, force_variant, variant, M):
+    """Sums beyond the FP16 range round to infinity of their sign (one RNE
+    cast); sums well inside it meet the bound; the band where the tolerance
+    can move a value across 65520 may give either."""
+    force_variant(variant)
+    g = wl.generator(420 + M)
+    N, K = 200, 1024
+    xv = np.abs(g.standard_normal((M, K))) * 4.0 + 1.0
+    xb = oracle.encode(xv, "f16")
+    t = wl.ternary_codes(g, N, K, 0.1)
+    t[: N // 4] = 1                                                    # sums of +2.7e5 or so
+    t[N // 4: N // 2] = -1                                             # and of -2.7e5
+    s = np.full((N, K // 128), np.float16(64.0), dtype=np.float16)   # sums of several 10^5
+    s[N // 2:] = np.float16(0.25)                                      # these stay finite
+    lin = wl.Linear("ovf", "ternary", M, N, K, "f16", "f16", xb, t, s, None)
+    Y, _ = run_linear(lin)
+    A, Mg = oracle_linear(lin)
+    lim = 65520.0
+    big = np.abs(A) > lim * 1.01
+    small = np.abs(A) < 65504.0 * 0.99
+    assert big.any() and small.any()
+    assert np.all(np.isinf(Y[big])) and np.all(np.sign(Y[big]) == np.sign(A[big]))
+    ok, worst, nfail = oracle.check(Y[small], A[small], Mg[small], "f16")
+    assert ok, f"{nfail} finite outputs outside the bound"
