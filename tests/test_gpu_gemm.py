@@ -556,3 +556,31 @@ def test_fp16_output_overflows_to_infinity(lb, force_variant, variant, M):
     assert np.all(np.isinf(Y[big])) and np.all(np.sign(Y[big]) == np.sign(A[big]))
     ok, worst, nfail = oracle.check(Y[small], A[small], Mg[small], "f16")
     assert ok, f"{nfail} finite outputs outside the bound"
+
+
+@pytest.mark.parametrize("variant,M", [(None, 4), ("small-split", 16), (None, 1), ("large-pair", 40),
+                                       ("large-wide", 40)])
+def test_non_finite_activations_propagate(lb, force_variant, variant, M):
+    """NaN and infinities in X give the oracle's non-finite outputs in place
+    (IEEE: infinity times a zero weight is NaN, opposite infinities add to
+    NaN); every other output meets the bound."""
+    force_variant(variant)
+    g = wl.generator(430 + M)
+    N, K = 160, 1024
+    xv = g.standard_normal((M, K))
+    xv[0, 5] = np.nan
+    if M > 1:
+        xv[1, 7] = np.inf
+    if M > 2:
+        xv[2, 9] = -np.inf
+        xv[2, 700] = np.inf
+    xb = oracle.encode(xv, "bf16")
+    t = wl.ternary_codes(g, N, K, 0.35)
+    s = wl.group_scales(g, N, K)
+    lin = wl.Linear("nonfinite", "ternary", M, N, K, "bf16", "f32", xb, t, s, None)
+    Y, _ = run_linear(lin)
+    with np.errstate(invalid="ignore"):               # the oracle's own inf - inf and inf * 0
+        A, Mg = oracle_linear(lin)
+        ok, worst, nfail = oracle.check(Y, A, Mg, "f32")
+    assert not np.isfinite(A[0]).any()
+    assert ok, f"{nfail} outputs differ (non-finite in place, finite within the bound)"
