@@ -584,3 +584,28 @@ def test_non_finite_activations_propagate(lb, force_variant, variant, M):
         ok, worst, nfail = oracle.check(Y, A, Mg, "f32")
     assert not np.isfinite(A[0]).any()
     assert ok, f"{nfail} outputs differ (non-finite in place, finite within the bound)"
+
+
+@pytest.mark.parametrize("variant,M", [(None, 4), ("small-split", 16), (None, 1), ("large-pair", 40),
+                                       ("large-wide", 40)])
+def test_invalid_ternary_code_acts_as_zero(lb, force_variant, variant, M):
+    """The INT2 pattern 10 (never written by the packer; what the base-3
+    transcoder writes for an invalid byte) is read by every GEMM path as t = 0."""
+    force_variant(variant)
+    g = wl.generator(440 + M)
+    N, K = 96, 1024
+    lin = wl.make_linear("code10", "ternary", M, N, K, seed=441 + M, p0=0.35)
+    packed = oracle.pack_ternary(lin.codes)
+    rows = g.choice(N, size=20, replace=False)
+    cols = g.choice(K // 4, size=20)
+    for r, c in zip(rows, cols):
+        packed[r, c] = 0xAA                                  # four fields of 10
+    t_eff, bad = oracle.unpack_ternary(packed, K)           # 10 -> 0, counted
+    assert bad == 80
+    x = dev_bits(lin.x, "bf16")
+    s = torch.from_numpy(lin.scales.view(np.int16)).cuda().view(torch.float16)
+    y = lb.gemm(x, torch.from_numpy(packed).cuda(), s, "ternary", out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    A = oracle.linear(lin.x, "bf16", t_eff, lin.scales)
+    Mg = oracle.magnitude(lin.x, "bf16", t_eff, lin.scales)
+    _assert_parity(to_host64(y), A, Mg, "f32", f"code 10 {variant}")
