@@ -16,13 +16,13 @@
  *    never allocates, frees or synchronises; work is enqueued on `stream`
  *    (a hipStream_t; NULL means the null stream) and runs asynchronously.
  *  - The return value reports argument errors (checked on the host before any
- *    launch) and launch errors (hipGetLastError after the launch).
+ *    launch) and launch errors (hipGetLastError after the launch). Errors
+ *    that happen later on the device surface at the caller's next
+ *    synchronisation, as for any HIP kernel.
  *  - Outputs may not overlap inputs (or, for lowbit_gemm_grouped, each other):
  *    the byte ranges each call addresses are compared on the host and an
  *    overlap returns LOWBIT_ERR_OVERLAP (lowbit_gelu alone may run in place,
- *    with in == out exactly). Errors
- *    that happen later on the device surface at the caller's next
- *    synchronisation, as for any HIP kernel.
+ *    with in == out exactly).
  *  - Matrices are row-major. Sizes are element counts unless stated.
  *  - The library runs on gfx950 only; other devices get LOWBIT_ERR_DEVICE.
  *  - Every call is stateless apart from a per-device cache of device
@@ -120,8 +120,10 @@ int32_t pack_ternary(const int8_t* codes, int64_t N, int64_t K, uint8_t* packed,
                      int32_t* invalid_count, void* stream);
 
 /* Pack int8 binary codes t[N][K] in {-1,+1} into the 1-bit layout above
- * (1 bit per binary weight, as on the hada.io page and in the "1.125 bits"
- * arithmetic of the ai-engineering page). packed: N*K/8 bytes. K % 32 == 0.
+ * (1 bit per binary weight: "Bonsai Image 4B 1-bit untuk pembuatan gambar di
+ * perangkat lokal", section on the two variants; the 1.125-bit arithmetic of
+ * "Introducing 1-bit and Ternary Bonsai Image 4B", section on the quantisation
+ * arithmetic). packed: N*K/8 bytes. K % 32 == 0.
  * Values other than -1/+1 are counted in invalid_count and packed as bit 0
  * (t = -1). Alignment and ownership as pack_ternary. */
 int32_t pack_binary(const int8_t* codes, int64_t N, int64_t K, uint8_t* packed,

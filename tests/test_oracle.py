@@ -212,17 +212,22 @@ def test_storage_sizes_exact():
 
 
 def test_effective_bits_match_printed_values():
-    # Binary: 1 bit + 16/128 bits of scale = 1.125 (printed on the hada.io page and
-    # in "量化数学" of the ai-engineering page). Storage of this library is the same.
+    # Binary: 1 bit + 16/128 bits of scale = 1.125 (printed on "Bonsai Image 4B 1-bit
+    # untuk pembuatan gambar di perangkat lokal", section on the two variants, and in
+    # "量化数学" of "Introducing 1-bit and Ternary Bonsai Image 4B"). Storage of this
+    # library is the same.
     N, K = 3072, 3072
     bits_bin = (oracle.packed_bytes("binary", N, K) + oracle.scale_bytes(N, K)) * 8 / (N * K)
     assert bits_bin == 1.125
     # Ternary information rate log2(3) + 16/128 ~= 1.71 (printed), and INT2 storage
-    # is 2 + 16/128 = 2.125 bits (2 bits per ternary, printed on the tailorednewshub page).
+    # is 2 + 16/128 = 2.125 bits (2 bits per ternary: "Cómo Bonsai Ternary 4B revoluciona
+    # la difusión texto-imagen", section "Representación y almacenamiento de los pesos
+    # ternarios").
     assert round(math.log2(3) + 16 / 128, 2) == 1.71
     bits_tern = (oracle.packed_bytes("ternary", N, K) + oracle.scale_bytes(N, K)) * 8 / (N * K)
     assert bits_tern == 2.125
-    # Layer-level reductions printed on the ai-engineering page: 16/1.125 ~ 14x, 16/1.71 ~ 9.4x
+    # Layer-level reductions printed in "量化数学" of "Introducing 1-bit and Ternary Bonsai
+    # Image 4B": 16/1.125 ~ 14x, 16/1.71 ~ 9.4x
     assert round(16 / 1.125) == 14
     assert round(16 / 1.71, 1) == 9.4
 
