@@ -64,7 +64,7 @@ def dev16(torch, bits, dtype):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(dtype)
 
 
-def bench_large(torch, lb, steps, warmup):
+def bench_large(torch, lb, steps, warmup, settle_s=0.0):
     import workloads as wl
     up, down = wl.config3()
     M, K1, N1, N2 = up.M, up.K, up.N, down.N
@@ -87,6 +87,16 @@ def bench_large(torch, lb, steps, warmup):
         if evs is not None:
             evs[2].record()
 
+    # The GPU's clock ramps up over the first fraction of a second of load:
+    # the step first runs untimed for settle_s seconds of wall time (in
+    # batches of 50), then the W warm-up steps, then the K timed steps.
+    settle_steps = 0
+    t_end = time.perf_counter() + settle_s
+    while time.perf_counter() < t_end:
+        for _ in range(50):
+            step()
+        settle_steps += 50
+        torch.cuda.synchronize()
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -111,8 +121,14 @@ def bench_large(torch, lb, steps, warmup):
     avg_launch_ms = float(np.mean(launches))
     up_ms = float(np.mean(launches[0::2]))
     down_ms = float(np.mean(launches[1::2]))
+
+    def spread(v):
+        return {"min": round(float(np.min(v)), 4), "median": round(float(np.median(v)), 4),
+                "max": round(float(np.max(v)), 4)}
     return dict(M=M, N1=N1, K1=K1, N2=N2, total_ms=total_ms, wall_s=wall, flop_step=flop_step,
-                flop_launch=flop_launch, avg_launch_ms=avg_launch_ms, up_ms=up_ms, down_ms=down_ms)
+                flop_launch=flop_launch, avg_launch_ms=avg_launch_ms, up_ms=up_ms, down_ms=down_ms,
+                settle_steps=settle_steps, up_spread=spread(launches[0::2]), down_spread=spread(launches[1::2]),
+                step_spread=spread([a + b for a, b in zip(launches[0::2], launches[1::2])]))
 
 
 def bench_dense(torch, M, N1, K1, N2, steps=50, warmup=50):
@@ -722,6 +738,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=300)
+    ap.add_argument("--settle-s", type=float, default=2.0,
+                    help="seconds of untimed steps before the warm-up steps, so the timed steps run at "
+                         "the clock the GPU settles to under this load")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-small", action="store_true")
     ap.add_argument("--no-context", action="store_true",
@@ -773,7 +792,7 @@ def main():
         print(json.dumps(cpu_configs(torch, lb)), flush=True)
         return
 
-    r = bench_large(torch, lb, args.steps, args.warmup)
+    r = bench_large(torch, lb, args.steps, args.warmup, args.settle_s)
     ms_step = r["total_ms"] / args.steps
     tflops = r["flop_step"] / (ms_step * 1e-3) / 1e12
     achieved = r["flop_launch"] / (r["avg_launch_ms"] * 1e-3) / 1e12
@@ -819,6 +838,8 @@ def main():
                       "(up: 96x256 tiles, two workgroups per CU; down: 128x512 tiles)",
             "avg_launch_ms": round(r["avg_launch_ms"], 4),
             "flop_per_launch": r["flop_launch"],
+            "launch_ms": {"up": r["up_spread"], "down": r["down_spread"], "step": r["step_spread"]},
+            "settle": {"seconds": args.settle_s, "untimed_steps": r["settle_steps"]},
         },
         "cpu_baseline": cpu,
         "dense_bf16_matmul": dense,

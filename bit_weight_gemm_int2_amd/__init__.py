@@ -38,6 +38,7 @@ SIGNATURES = [
     ("lowbit_abi_version", _I32, []),
     ("lowbit_status_string", ctypes.c_char_p, [_I32]),
     ("lowbit_init", _I32, []),
+    ("lowbit_debug_force_variant", _I32, [ctypes.c_char_p]),
     ("lowbit_packed_bytes", _I64, [_I32, _I64, _I64]),
     ("lowbit_scale_count", _I64, [_I64, _I64, _I32]),
     ("pack_ternary", _I32, [_P, _I64, _I64, _P, _P, _P]),
@@ -108,24 +109,45 @@ def workspace_bytes(fmt, M: int, N: int, K: int) -> int:
     return int(lib().lowbit_gemm_workspace_bytes(_FMT[fmt], M, N, K))
 
 
+def force_variant(name=None):
+    """Test hook: force one kernel family ("large", "small", "large-wide",
+    "large-pair", "small-split") for every later call of the process, or
+    restore the automatic choice with None / "auto"."""
+    _check(lib().lowbit_debug_force_variant(None if name is None else name.encode()), "lowbit_debug_force_variant")
+
+
 _WORKSPACES = {}
 
 
-def new_workspace(nbytes: int, device=None) -> torch.Tensor:
+def new_workspace(nbytes: int, device=None, stream=None) -> torch.Tensor:
     """A workspace for lowbit_gemm: zeroed device bytes (the library returns
-    its counters to zero after every call, so it stays reusable)."""
-    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device or "cuda")
+    its counters to zero after every call, so it stays reusable). The zeros
+    are written on `stream` (default: the current stream), the stream the
+    workspace is then used on."""
+    dev = torch.device(device or "cuda")
+    st = stream if stream is not None else torch.cuda.current_stream(dev)
+    with torch.cuda.stream(st):
+        ws = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=dev)
+        ws.zero_()
+    return ws
 
 
-def _shared_workspace(device: torch.device, nbytes: int) -> torch.Tensor:
-    """A workspace per device, reused by every call that passes none (calls
-    on one stream never overlap). It grows when a larger problem needs more;
-    grow it before any HIP graph capture by running the largest problem once."""
+def _shared_workspace(device: torch.device, nbytes: int, stream) -> torch.Tensor:
+    """A workspace per (device, stream), reused by every call on that stream
+    that passes none: calls on one stream never overlap, and calls on two
+    streams never share one. It is zeroed on the stream it serves, and grows
+    when a larger problem needs more (the buffer it replaces is kept alive
+    until the work queued on the stream so far is done); grow it before any
+    HIP graph capture by running the largest problem once."""
     idx = device.index if device.index is not None else torch.cuda.current_device()
-    ws = _WORKSPACES.get(idx)
+    st = stream if stream is not None else torch.cuda.current_stream(idx)
+    key = (idx, st.cuda_stream)
+    ws = _WORKSPACES.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = new_workspace(max(nbytes, 1 << 20), device)
-        _WORKSPACES[idx] = ws
+        if ws is not None:
+            ws.record_stream(st)
+        ws = new_workspace(max(nbytes, 1 << 20), torch.device("cuda", idx), st)
+        _WORKSPACES[key] = ws
     return ws
 
 
@@ -239,7 +261,7 @@ def gemm(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, fmt, bias:
         raise ValueError(f"out must be [{M}, {N}] with unit stride along N")
     ws_need = workspace_bytes(fmt, M, N, K)
     if ws_need and workspace is None:
-        workspace = _shared_workspace(x.device, ws_need)
+        workspace = _shared_workspace(x.device, ws_need, stream)
     elif ws_need and workspace.numel() * workspace.element_size() < ws_need:
         raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, "
                          f"lowbit_gemm needs {ws_need}")
@@ -298,7 +320,7 @@ def gemm_grouped(xs, packeds, scales, fmt, biases=None, out_dtype: Optional[torc
         bdt = _DT[biases[0].dtype]
     need = int(lib().lowbit_gemm_grouped_workspace_bytes(count, _FMT[fmt], M, N, K))
     if need and workspace is None:
-        workspace = _shared_workspace(x0.device, need)
+        workspace = _shared_workspace(x0.device, need, stream)
     elif need and workspace.numel() * workspace.element_size() < need:
         raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, "
                          f"lowbit_gemm_grouped needs {need}")

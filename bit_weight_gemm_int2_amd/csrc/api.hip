@@ -69,15 +69,32 @@ bool overlaps(const void* p, int64_t bytes, const void* q, int64_t qbytes) {
   return a < b + (uintptr_t)qbytes && b < a + (uintptr_t)bytes;
 }
 
-int force_variant() {
-  const char* v = std::getenv("LOWBIT_FORCE_VARIANT");
-  if (!v) return 0;
+// Kernel-family test hook: -1 for a name that is not one.
+int parse_variant(const char* v) {
+  if (!v || !*v || !std::strcmp(v, "auto")) return 0;
   if (!std::strcmp(v, "large")) return 1;
   if (!std::strcmp(v, "small")) return 2;
   if (!std::strcmp(v, "large-wide")) return 5;
   if (!std::strcmp(v, "large-pair")) return 6;
   if (!std::strcmp(v, "small-split")) return 7;
-  return 0;
+  return -1;
+}
+
+// The forced kernel family: LOWBIT_FORCE_VARIANT, read once per process (an
+// unknown name counts as unset), unless lowbit_debug_force_variant set it.
+std::atomic<int> g_variant{0};
+std::once_flag g_variant_once;
+
+void read_variant_env() {
+  std::call_once(g_variant_once, [] {
+    const int v = parse_variant(std::getenv("LOWBIT_FORCE_VARIANT"));
+    g_variant.store(v < 0 ? 0 : v, std::memory_order_relaxed);
+  });
+}
+
+int force_variant() {
+  read_variant_env();
+  return g_variant.load(std::memory_order_relaxed);
 }
 
 constexpr int64_t kMaxDim = (int64_t)1 << 31;
@@ -108,6 +125,14 @@ const char* lowbit_status_string(int32_t s) {
 }
 
 int32_t lowbit_init(void) { return current_device(nullptr); }
+
+int32_t lowbit_debug_force_variant(const char* name) {
+  const int v = parse_variant(name);
+  if (v < 0) return LOWBIT_ERR_DTYPE;
+  read_variant_env();
+  g_variant.store(v, std::memory_order_relaxed);
+  return LOWBIT_OK;
+}
 
 int64_t lowbit_packed_bytes(int32_t format, int64_t N, int64_t K) {
   if (N < 1 || K < 1 || N >= kMaxDim || K >= kMaxDim) return -1;
@@ -254,6 +279,18 @@ int64_t y_span(int64_t M, int64_t N, int64_t ldy, int32_t y_dtype) {
   return ((M - 1) * ldy + N) * (y_dtype == LOWBIT_F32 ? 4 : 2);
 }
 
+// Does a workspace of `need` bytes share a byte with any operand of one
+// problem? (The kernels write partial sums and counters into it.)
+bool workspace_overlaps(const void* ws, size_t need, int32_t format, const void* X, int64_t M, int64_t K,
+                        int64_t ldx, const uint8_t* W, const void* scales, int64_t N, const void* bias,
+                        int32_t bias_dtype, const void* Y, int32_t y_dtype, int64_t ldy) {
+  const int64_t n = (int64_t)need;
+  const int64_t wrow = format == LOWBIT_TERNARY_INT2 ? K / 4 : K / 8;
+  return overlaps(ws, n, Y, y_span(M, N, ldy, y_dtype)) || overlaps(ws, n, X, ((M - 1) * ldx + K) * 2) ||
+         overlaps(ws, n, W, N * wrow) || overlaps(ws, n, scales, N * (K / 128) * 2) ||
+         overlaps(ws, n, bias, N * (bias_dtype == LOWBIT_F32 ? 4 : 2));
+}
+
 lowbit::GemmArgs make_args(int32_t format, int64_t K, int64_t ldx, const uint8_t* W_packed, const void* scales,
                            int64_t N, const void* bias, int32_t bias_dtype, int32_t y_dtype, int64_t ldy,
                            int32_t activation, void* workspace) {
@@ -304,15 +341,17 @@ int32_t lowbit_gemm(int32_t format, const void* X, int32_t x_dtype, int64_t M, i
   int32_t st = check_problem(format, X, x_dtype, M, K, ldx, W_packed, scales, group, N, bias, bias_dtype, Y,
                              y_dtype, ldy, activation, &rows_max);
   if (st) return st;
+  // the whole workspace the caller hands over is scratch: none of its bytes
+  // may belong to an operand (checked before the device, whatever is needed)
+  if (workspace && workspace_overlaps(workspace, workspace_bytes, format, X, M, K, ldx, W_packed, scales, N, bias,
+                                      bias_dtype, Y, y_dtype, ldy))
+    return LOWBIT_ERR_OVERLAP;
   int num_cu = 0;
   st = current_device(&num_cu);
   if (st) return st;
   size_t need = lowbit_gemm_workspace_bytes(format, M, N, K);
   if (need && (!workspace || workspace_bytes < need)) return LOWBIT_ERR_WORKSPACE;
   if (need && !aligned(workspace, 256)) return LOWBIT_ERR_ALIGN;
-  if (need && (overlaps(workspace, (int64_t)need, Y, y_span(M, N, ldy, y_dtype)) ||
-               overlaps(workspace, (int64_t)need, X, ((M - 1) * ldx + K) * 2)))
-    return LOWBIT_ERR_OVERLAP;
   const lowbit::GemmArgs a = make_args(format, K, ldx, W_packed, scales, N, bias, bias_dtype, y_dtype, ldy,
                                        activation, workspace);
   return run_problem(format, X, x_dtype, M, K, ldx, a, Y, y_dtype, ldy, rows_max, num_cu, force_variant(), stream);
@@ -358,6 +397,11 @@ int32_t lowbit_gemm_grouped(int32_t count, int32_t format, const void* const* X,
           (bias && overlaps(Y[z], yb, bias[u], N * (bias_dtype == LOWBIT_F32 ? 4 : 2))))
         return LOWBIT_ERR_OVERLAP;
     }
+  // the whole workspace is scratch: no byte of it may belong to any problem
+  for (int z = 0; workspace && z < count; ++z)
+    if (workspace_overlaps(workspace, workspace_bytes, format, X[z], M, K, ldx, W_packed[z], scales[z], N,
+                           bias ? bias[z] : nullptr, bias_dtype, Y[z], y_dtype, ldy))
+      return LOWBIT_ERR_OVERLAP;
   int num_cu = 0;
   int32_t st = current_device(&num_cu);
   if (st) return st;

@@ -331,23 +331,28 @@ __global__ __launch_bounds__(64 * WN) void gemm_large_kernel(GemmArgs a, int til
 //    b + {0..15} and b + {32..47} with b = {0, 64, 16, 80}[q], which is what
 //    the lane exchange leaves in its registers.
 //  * With one split the result is stored directly. Otherwise every workgroup
-//    writes its FP32 partial tile with agent-scope stores, waits for them,
-//    and takes a ticket for its column tile (agent-scope atomic add); the
-//    workgroup that takes the last ticket reads the partials back with
-//    agent-scope loads, sums them in split order (deterministic), applies
-//    bias and activation, stores Y and resets the ticket to zero. Only
-//    atomic-scope accesses touch the partials and tickets, so no L2
-//    writeback or invalidate is needed.
+//    writes its FP32 partial tile as 64-bit atomic words whose zero bits mean
+//    "not written" and takes a ticket for its column tile (agent-scope atomic
+//    add); the workgroup that takes the last ticket reads the other splits'
+//    words (polling any not yet written), sums the splits in split order
+//    (deterministic), stores zeros back, applies bias and activation, stores
+//    Y and resets the ticket to zero (details at the combine below).
 // ===========================================================================
 namespace stream {
 constexpr int MAXGS = 32;                      // groups per workgroup slice
 constexpr int MAXSPLIT = 16;                   // K splits
 __host__ __device__ constexpr size_t lds_bytes(int gs) { return (size_t)gs * 16 * 256; }
 // workspace: one 32-bit ticket per column tile in a fixed region at the
-// start (so calls of any shape reuse the same, zero, counters), then the FP32
-// partials [splits][M][N]
+// start (so calls of any shape reuse the same, zero, counters; its last word
+// counts bounded waits that gave up, which never happens in a correct run),
+// then the FP32 partials [splits][tiles][waves][lanes][4]
 constexpr int MAXTILES = 16384;
+constexpr int ERR_SLOT = MAXTILES - 1;
 constexpr size_t TICKET_BYTES = (size_t)MAXTILES * 4;
+// polls of a partial word before a wait gives up (about a quarter second)
+constexpr uint32_t POLL_LIMIT = 1u << 22;
+// a 64-bit partial word holds two written values (zero bits mean unwritten)
+__device__ __forceinline__ bool written(uint64_t w) { return (uint32_t)w != 0u && (uint32_t)(w >> 32) != 0u; }
 // K parts per workgroup: the largest KH <= 4 with WC * KH <= 16 waves and
 // whole blocks of four groups per part (GS % 4 KH == 0)
 __host__ __device__ constexpr int kparts(int wc, int gs) {
@@ -516,9 +521,23 @@ __global__ __launch_bounds__(64 * WC * stream::kparts(WC, GS)) void gemm_stream_
     }
     return;
   }
-  // partial tiles, lane-major: [split][tile][wave][lane] x 4 floats, written
-  // and read as two 64-bit agent-scope atomics per lane
-  // (the tiles of the problems of a grouped launch side by side)
+  // Partial tiles, lane-major: [split][tile][wave][lane] x 4 FP32 values (the
+  // tiles of the problems of a grouped launch side by side), written and read
+  // as two 64-bit agent-scope atomic words per lane. Every slot holds bits 0
+  // except while it carries a partial that its reducer has not yet consumed:
+  // a writer stores +0.0 as -0.0 (bits 0x80000000; a sum is unchanged by
+  // it), so a word whose halves are both nonzero is always the value its own
+  // split wrote in this launch. Each workgroup stores its partial, waits for
+  // the stores, then takes a ticket for its column tile; the one that takes
+  // the last ticket reads the other splits' words, polls any that do not yet
+  // read as written (a bounded wait), adds the splits in split order (its
+  // own from registers) and stores zeros over every split's words
+  // (consumed). Every value crosses between workgroups inside one 64-bit
+  // atomic object, so the result does not depend on ordering between
+  // different locations and needs no cache-wide fence: a reader cannot see
+  // an older value of a word than the zero its last consumer stored, since
+  // that store happened before this launch began. (The wait before the
+  // ticket only makes the first read succeed in practice.)
   const int wtile = GRP ? blockIdx.z * gridDim.x + tile : tile;
   int* ticket = (int*)a.ws + wtile;
   uint64_t* part = (uint64_t*)((uint8_t*)a.ws + stream::TICKET_BYTES);
@@ -526,35 +545,74 @@ __global__ __launch_bounds__(64 * WC * stream::kparts(WC, GS)) void gemm_stream_
   const int64_t my = (int64_t)(wtile * WC + cwv) * 64 + lane;
   if (lead) {
     uint64_t* dst = part + 2 * ((int64_t)split * tile_lanes + my);
-    __hip_atomic_store(dst, __builtin_bit_cast(uint64_t, f32x2{acc[0], acc[1]}), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(dst + 1, __builtin_bit_cast(uint64_t, f32x2{acc[2], acc[3]}), __ATOMIC_RELAXED,
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      // (through a scalar: __builtin_bit_cast of a vector element
+      // subscript reads element 0 with this compiler)
+      const float v = acc[e];
+      w[e] = __builtin_bit_cast(uint32_t, v);
+      w[e] = w[e] ? w[e] : 0x80000000u;
+    }
+    __hip_atomic_store(dst, (uint64_t)w[0] | ((uint64_t)w[1] << 32), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(dst + 1, (uint64_t)w[2] | ((uint64_t)w[3] << 32), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
   }
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);                        // partial stores complete
+  __builtin_amdgcn_s_waitcnt(0);                        // this wave's stores have completed
   __syncthreads();
   if (tid == 0)
     last_flag = __hip_atomic_fetch_add(ticket, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == splits - 1;
   __syncthreads();
   if (!last_flag || !lead) return;
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  // all partial loads in flight at once, then the sum in split order
+  // the reducer: every other split's loads in flight at once, then the
+  // bounded poll of any word not yet read as written
   uint64_t pv[stream::MAXSPLIT][2];
 #pragma unroll
   for (int t = 0; t < stream::MAXSPLIT; ++t) {
-    const uint64_t* src = part + 2 * ((int64_t)min(t, splits - 1) * tile_lanes + my);
-    pv[t][0] = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    pv[t][1] = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (t < splits && t != split) {
+      const uint64_t* src = part + 2 * ((int64_t)t * tile_lanes + my);
+      pv[t][0] = __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      pv[t][1] = __hip_atomic_load(src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  bool stuck = false;
+#pragma unroll
+  for (int t = 0; t < stream::MAXSPLIT; ++t) {
+    if (t < splits && t != split) {
+      const uint64_t* src = part + 2 * ((int64_t)t * tile_lanes + my);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        for (uint32_t n = 0; !stream::written(pv[t][h]); ++n) {
+          if (n == stream::POLL_LIMIT) {
+            stuck = true;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+          pv[t][h] = __hip_atomic_load(src + h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+    }
   }
   f32x4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int t = 0; t < stream::MAXSPLIT; ++t) {
     if (t < splits) {
-      const f32x2 lo = __builtin_bit_cast(f32x2, pv[t][0]), hi = __builtin_bit_cast(f32x2, pv[t][1]);
-      sum += f32x4{lo[0], lo[1], hi[0], hi[1]};
+      if (t == split) {
+        sum += acc;
+      } else {
+        sum += f32x4{__builtin_bit_cast(float, (uint32_t)pv[t][0]), __builtin_bit_cast(float, (uint32_t)(pv[t][0] >> 32)),
+                     __builtin_bit_cast(float, (uint32_t)pv[t][1]), __builtin_bit_cast(float, (uint32_t)(pv[t][1] >> 32))};
+      }
     }
   }
+  // consumed: plain 16-byte stores suffice, since nothing in this launch
+  // reads these words again and the next launch that uses the workspace
+  // starts after this one has ended
+#pragma unroll
+  for (int t = 0; t < stream::MAXSPLIT; ++t) {
+    if (t < splits) *(u32x4*)(part + 2 * ((int64_t)t * tile_lanes + my)) = u32x4{0u, 0u, 0u, 0u};
+  }
+  if (stuck) __hip_atomic_fetch_add((int*)a.ws + stream::ERR_SLOT, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (col_ok) {
     const float b = a.bias ? load_bias(a.bias, a.bias_dtype, n) : 0.0f;
 #pragma unroll
@@ -828,7 +886,7 @@ static bool stream_plan(int M, int N, int K, int num_cu, StreamPlan* out, int co
   StreamPlan bp{};
   for (int wc : {3, 4, 5, 6, 8}) {
   const int tiles = (N + 16 * wc - 1) / (16 * wc);
-  if ((int64_t)tiles * count > stream::MAXTILES) continue;
+  if ((int64_t)tiles * count > stream::ERR_SLOT) continue;            // tickets below the error word
   for (int sp = 1; sp <= min(stream::MAXSPLIT, G); ++sp) {
     const int gps = (G + sp - 1) / sp;
     if (gps > stream::MAXGS) continue;

@@ -27,13 +27,9 @@
  *  - The library runs on gfx950 only; other devices get LOWBIT_ERR_DEVICE.
  *  - Every call is stateless apart from a per-device cache of device
  *    properties, and is safe to call from several host threads.
- *  - Test hook: the environment variable LOWBIT_FORCE_VARIANT, read on every
- *    call, forces one kernel family so that tests reach every launch path:
- *    "large" (the large-M kernel at any M), "small" (the small-M kernels
- *    only), "large-wide" / "large-pair" (one large-M tile configuration),
- *    "small-split" (the small-M column-tile kernel with its K split across
- *    workgroups). Results keep the same accuracy contract under every
- *    variant, and the workspace queries follow it; leave it unset otherwise.
+ *  - Test hook: lowbit_debug_force_variant (below) forces one kernel family
+ *    so that tests reach every launch path; the environment variable
+ *    LOWBIT_FORCE_VARIANT, read once per process, sets its initial value.
  *
  * Packed weight layout (this library's own; the pages fix only "2 bits per
  * ternary" and "1 bit per binary weight")
@@ -100,6 +96,19 @@ const char* lowbit_status_string(int32_t status);
 /* Check that the current device is gfx950 and cache its properties.
  * Optional: every entry point does the same on first use. */
 int32_t lowbit_init(void);
+
+/* Test hook, for tests only: force one kernel family for every later call of
+ * the process (all threads), so that tests reach every launch path on the
+ * same shapes. name: "auto" or NULL (the automatic choice), "large" (the
+ * large-M kernel at any M), "small" (the small-M kernels only), "large-wide"
+ * / "large-pair" (one large-M tile configuration), "small-split" (the
+ * small-M column-tile kernel with its K split across workgroups). Results
+ * keep the same accuracy contract under every variant, and the workspace
+ * queries follow it. The initial value comes from the environment variable
+ * LOWBIT_FORCE_VARIANT, read once. Returns LOWBIT_ERR_DTYPE for an unknown
+ * name (the setting is then unchanged). Not for concurrent use with calls on
+ * other threads that depend on the automatic choice. */
+int32_t lowbit_debug_force_variant(const char* name);
 
 /* Bytes of packed codes for an N x K matrix: N*K/4 (ternary), N*K/8 (binary),
  * N*ceil(K/5) (base-3); -1 for a bad format or a K that breaks the packing
@@ -172,7 +181,13 @@ size_t lowbit_gemm_workspace_bytes(int32_t format, int64_t M, int64_t N, int64_t
  * with FP32 accumulation, then one round-to-nearest-even cast to y_dtype.
  * Accuracy contract per element: |Y - exact| <= 1e-3 * (sum_k |x_k w_k| +
  * |bias|) + 1e-5, plus half an output ulp for FP16/BF16 outputs (before the
- * activation; GELU is then applied to the FP32 value).
+ * activation; GELU is then applied to the FP32 value). Range limit: the
+ * kernels accumulate each 128-group's sum of x * (2t) in FP32 and rescale
+ * between groups by ratios of the group scales, so the contract holds while
+ * 2 * sum_k |x_k| * max_g |s_g| / min_g |s_g| (over a row's nonzero scales)
+ * stays below about 2^100; FP16 activations always do, BF16 activations of
+ * magnitude near 2^120 with scales spread by 2^30 could overflow to inf
+ * where the exact result is finite.
  *
  *   format      LOWBIT_TERNARY_INT2 or LOWBIT_BINARY_1BIT (base-3 weights
  *               are transcoded first with base3_to_int2; LOWBIT_TERNARY_BASE3
@@ -197,7 +212,9 @@ size_t lowbit_gemm_workspace_bytes(int32_t format, int64_t M, int64_t N, int64_t
  *               be zero before the first call that uses it (allocate it
  *               zeroed); every call leaves the counters it used at zero
  *               again, so it can be reused without clearing. Calls that can
- *               run concurrently (other streams) must not share it.
+ *               run concurrently (other streams) must not share it. None of
+ *               its workspace_bytes bytes may belong to X, W, scales, bias or
+ *               Y (LOWBIT_ERR_OVERLAP, checked for any non-NULL workspace)
  *   M, N, K     M, N >= 1; K >= 128 and K % 128 == 0; M, N, K < 2^31
  *
  * Ternary codes 10 are not checked here (hot path); they act as t = 0.

@@ -32,7 +32,8 @@ def test_header_declares_expected_entry_points():
     for want in ("pack_ternary", "pack_binary", "pack_base3", "unpack_lowbit", "base3_to_int2",
                  "lowbit_gemm", "lowbit_gemm_grouped", "lowbit_gemm_grouped_workspace_bytes",
                  "lowbit_gemm_workspace_bytes", "lowbit_packed_bytes", "lowbit_scale_count",
-                 "lowbit_status_string", "lowbit_abi_version", "lowbit_init", "lowbit_gelu"):
+                 "lowbit_status_string", "lowbit_abi_version", "lowbit_init", "lowbit_gelu",
+                 "lowbit_debug_force_variant"):
         assert want in names
 
 
@@ -155,9 +156,36 @@ def test_argument_errors_before_any_device_work(L):
     assert L.pack_ternary(PX, 4, 16, PW, PX + 2, None) == b.ERR_ALIGN    # counter checked for alignment first
     assert L.pack_ternary(PX, 4, 16, PW, PX + 16, None) == b.ERR_OVERLAP  # then for overlap
     assert L.lowbit_gelu(PX, PX + 16, b.BF16, 100, None) == b.ERR_OVERLAP
+    # a workspace may share no byte with any operand (its declared size is checked)
+    for where in (PX, PX + 256 * 2 * 15, PW + 512, PS, PY + 64):
+        assert call(ws=where - 256, wsb=512) == b.ERR_OVERLAP, hex(where)
+    assert call(ws=PB, wsb=256, bias=PB + 128, bd=b.F32) == b.ERR_OVERLAP
+    for z in (0, 1):
+        for where in (PX, PW, PS):
+            ins = [PX + (1 << 30), PX + (2 << 30)]
+            ins[z] = where
+            kw = dict(X=arr(*ins)) if where == PX else dict(W=arr(*ins)) if where == PW else dict(S=arr(*ins))
+            X = kw.get("X", arr(PX + (1 << 30), PX + (2 << 30)))
+            W = kw.get("W", arr(PW, PW))
+            S = kw.get("S", arr(PS, PS))
+            assert L.lowbit_gemm_grouped(2, b.TERNARY, X, b.BF16, 16, 256, 256, W, S, 128, 64, None, b.NONE,
+                                         arr(PY, PY + (1 << 30)), b.BF16, 64, 0, where, 256, None) == b.ERR_OVERLAP
+        assert L.lowbit_gemm_grouped(2, b.TERNARY, arr(PX, PX), b.BF16, 16, 256, 256, arr(PW, PW), arr(PS, PS), 128,
+                                     64, None, b.NONE, arr(PY, PY + (1 << 30)), b.BF16, 64, 0,
+                                     [PY, PY + (1 << 30)][z] + 32, 64, None) == b.ERR_OVERLAP
     assert L.lowbit_gemm_grouped_workspace_bytes(0, b.TERNARY, 16, 64, 256) == 0
     assert L.lowbit_gemm_grouped_workspace_bytes(9, b.TERNARY, 16, 64, 256) == 0
     assert L.lowbit_gelu(P, P, b.NONE, 10, None) == b.ERR_DTYPE
+
+
+def test_variant_hook_names(L):
+    """The test hook takes exactly the documented names; an unknown one is
+    refused and leaves the setting alone."""
+    import bit_weight_gemm_int2_amd as b
+    for name in (b"large", b"small", b"large-wide", b"large-pair", b"small-split", b"auto", None):
+        assert L.lowbit_debug_force_variant(name) == b.OK
+    assert L.lowbit_debug_force_variant(b"bogus") == b.ERR_DTYPE
+    b.force_variant(None)
 
 
 @pytest.mark.skipif(__import__("torch").cuda.device_count() > 0, reason="checks the no-GPU answer")

@@ -29,16 +29,9 @@ def _assert_parity(Y, A, Mg, y_dtype, what):
 
 
 @pytest.fixture
-def force_variant():
-    old = os.environ.get("LOWBIT_FORCE_VARIANT")
-
-    def set_(v):
-        if v is None:
-            os.environ.pop("LOWBIT_FORCE_VARIANT", None)
-        else:
-            os.environ["LOWBIT_FORCE_VARIANT"] = v
-    yield set_
-    set_(old)
+def force_variant(lb):
+    yield lb.force_variant
+    lb.force_variant(None)
 
 
 # ------------------------------------------------------------- workloads ---
@@ -282,7 +275,8 @@ def test_split_k_small_m_is_deterministic_and_reusable(lb, force_variant, fmt, M
     through the workspace, and the last one resets its counter. Forty calls in
     a row on one workspace (each into a NaN-filled output) must all write every
     element and give identical bits; a workspace smaller than required is
-    refused."""
+    refused. Afterwards the whole workspace is zero again: tickets, the
+    counter of bounded waits that gave up, and every partial slot."""
     force_variant("small-split")
     need = lb.workspace_bytes(fmt, M, N, K)
     assert need > 0                                   # these shapes split K
@@ -299,7 +293,9 @@ def test_split_k_small_m_is_deterministic_and_reusable(lb, force_variant, fmt, M
     assert not torch.isnan(outs[0]).any()
     for o in outs[1:]:
         assert torch.equal(o.view(torch.int32), outs[0].view(torch.int32))
-    assert int(ws.count_nonzero()) >= 0                # still a valid tensor
+    # every ticket, the give-up counter and every partial slot are zero again
+    # (each reducer stores zeros over the partials it consumed)
+    assert int(ws.count_nonzero()) == 0
     A, Mg = oracle_linear(lin)
     _assert_parity(to_host64(outs[0]), A, Mg, "f32", "split-K small M")
     with pytest.raises(ValueError):

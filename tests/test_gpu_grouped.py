@@ -85,8 +85,7 @@ def test_grouped_split_k_workspace_and_determinism(lb):
     by side in one workspace, come back to zero, and a second call gives the
     same bits."""
     banner("grouped split-K workspace")
-    old = os.environ.get("LOWBIT_FORCE_VARIANT")
-    os.environ["LOWBIT_FORCE_VARIANT"] = "small-split"
+    lb.force_variant("small-split")
     try:
         lins = _problems(3, "ternary", 16, 2048, 12288, seed=7200)
         need = lb.lib().lowbit_gemm_grouped_workspace_bytes(3, lb.TERNARY, 16, 2048, 12288)
@@ -94,15 +93,12 @@ def test_grouped_split_k_workspace_and_determinism(lb):
         ws = lb.new_workspace(need)
         Ys, _ = _run(lb, lins, workspace=ws)
         _check(lins, Ys, "bf16")
-        assert int(ws[: 64 * 1024].count_nonzero()) == 0
+        assert int(ws.count_nonzero()) == 0     # tickets and partial slots
         Ys2, _ = _run(lb, lins, workspace=ws)
         for a, b in zip(Ys, Ys2):
             assert np.array_equal(a, b)
     finally:
-        if old is None:
-            os.environ.pop("LOWBIT_FORCE_VARIANT", None)
-        else:
-            os.environ["LOWBIT_FORCE_VARIANT"] = old
+        lb.force_variant(None)
 
 
 def test_one_problem_group_equals_lowbit_gemm(lb):
@@ -153,14 +149,10 @@ def test_grouped_under_forced_variants(lb, variant):
     """Every kernel family a group can land on: forced large-M kernels run the
     problems one launch each even at M <= 16; forced small-M kernels group them."""
     banner(f"grouped forced {variant}")
-    old = os.environ.get("LOWBIT_FORCE_VARIANT")
-    os.environ["LOWBIT_FORCE_VARIANT"] = variant
+    lb.force_variant(variant)
     try:
         lins = _problems(3, "binary", 16, 1000, 4608, seed=7500)
         Ys, _ = _run(lb, lins)
         _check(lins, Ys, "bf16")
     finally:
-        if old is None:
-            os.environ.pop("LOWBIT_FORCE_VARIANT", None)
-        else:
-            os.environ["LOWBIT_FORCE_VARIANT"] = old
+        lb.force_variant(None)

@@ -62,11 +62,10 @@ CASES = [  # (forced variant, fmt, M, N, K, y dtype, row padding)
 @pytest.mark.parametrize("variant,fmt,M,N,K,yd,pad", CASES)
 def test_gemm_writes_only_its_output(lb, variant, fmt, M, N, K, yd, pad):
     banner(f"guards {variant} {fmt} {M}x{N}x{K} -> {yd}")
-    old = os.environ.get("LOWBIT_FORCE_VARIANT")
     if variant:
-        os.environ["LOWBIT_FORCE_VARIANT"] = variant
+        lb.force_variant(variant)
     else:
-        os.environ.pop("LOWBIT_FORCE_VARIANT", None)
+        lb.force_variant(None)
     try:
         lin = wl.make_linear("guard", fmt, M, N, K, seed=950 + M, p0=0.35, with_bias=True)
         x = dev_bits(lin.x, "bf16")
@@ -86,10 +85,7 @@ def test_gemm_writes_only_its_output(lb, variant, fmt, M, N, K, yd, pad):
         ok, worst, nfail = oracle.check(to_host64(y.contiguous()), A, Mg, yd)
         assert ok, f"{nfail} outside the bound"
     finally:
-        if old is None:
-            os.environ.pop("LOWBIT_FORCE_VARIANT", None)
-        else:
-            os.environ["LOWBIT_FORCE_VARIANT"] = old
+        lb.force_variant(None)
 
 
 def test_grouped_writes_only_its_outputs(lb):

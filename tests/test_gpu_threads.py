@@ -45,7 +45,8 @@ def test_concurrent_host_threads(lb):
     def worker(tid):
         try:
             st = torch.cuda.Stream()
-            wss = [lb.new_workspace(lb.workspace_bytes(fmt, M, N, K)) for fmt, M, N, K, *_ in ops]
+            # zeroed on the stream that uses them
+            wss = [lb.new_workspace(lb.workspace_bytes(fmt, M, N, K), stream=st) for fmt, M, N, K, *_ in ops]
             with torch.cuda.stream(st):
                 outs = []
                 for r in range(12):
