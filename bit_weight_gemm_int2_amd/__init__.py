@@ -53,6 +53,8 @@ SIGNATURES = [
     ("lowbit_gemm_grouped", _I32, [_I32, _I32, _P, _I32, _I64, _I64, _I64, _P, _P, _I32, _I64,
                                    _P, _I32, _P, _I32, _I64, _I32, _P, _SZ, _P]),
     ("lowbit_gemm_grouped_workspace_bytes", _SZ, [_I32, _I32, _I64, _I64, _I64]),
+    ("lowbit_gemm_noalloc", _I32, [_I32, _P, _I32, _I64, _I64, _I64, _P, _P, _I32, _I64,
+                                   _P, _I32, _P, _I32, _I64, _I32, _P]),
 ]
 MAX_GROUP = 8
 

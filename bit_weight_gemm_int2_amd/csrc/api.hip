@@ -97,6 +97,31 @@ int force_variant() {
   return g_variant.load(std::memory_order_relaxed);
 }
 
+// Scratch of the allocation-free entry point: one array per GPU, for the
+// life of the process (split-K counters, then partial sums). Host code never
+// uses the array's name as an address: each device's copy is looked up once
+// with hipGetSymbolAddress, with that device current, and kept below.
+static __device__ __align__(256) uint8_t scratch[LOWBIT_NOALLOC_SCRATCH_BYTES];
+
+std::atomic<void*> g_scratch[kMaxDevices];
+
+// The current device's scratch address (looked up on first use per device).
+int32_t scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LOWBIT_ERR_DEVICE;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return LOWBIT_ERR_HIP;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return LOWBIT_OK;
+}
+
 constexpr int64_t kMaxDim = (int64_t)1 << 31;
 // largest operand byte span the kernels' 32-bit offsets cover (with room
 // for the last 16-byte load)
@@ -124,7 +149,12 @@ const char* lowbit_status_string(int32_t s) {
   }
 }
 
-int32_t lowbit_init(void) { return current_device(nullptr); }
+int32_t lowbit_init(void) {
+  int32_t st = current_device(nullptr);
+  if (st) return st;
+  void* p = nullptr;
+  return scratch_address(&p);
+}
 
 int32_t lowbit_debug_force_variant(const char* name) {
   const int v = parse_variant(name);
@@ -354,6 +384,29 @@ int32_t lowbit_gemm(int32_t format, const void* X, int32_t x_dtype, int64_t M, i
   if (need && !aligned(workspace, 256)) return LOWBIT_ERR_ALIGN;
   const lowbit::GemmArgs a = make_args(format, K, ldx, W_packed, scales, N, bias, bias_dtype, y_dtype, ldy,
                                        activation, workspace);
+  return run_problem(format, X, x_dtype, M, K, ldx, a, Y, y_dtype, ldy, rows_max, num_cu, force_variant(), stream);
+}
+
+int32_t lowbit_gemm_noalloc(int32_t format, const void* X, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx,
+                            const uint8_t* W_packed, const void* scales, int32_t group, int64_t N,
+                            const void* bias, int32_t bias_dtype, void* Y, int32_t y_dtype, int64_t ldy,
+                            int32_t activation, void* stream) {
+  int64_t rows_max = 0;
+  int32_t st = check_problem(format, X, x_dtype, M, K, ldx, W_packed, scales, group, N, bias, bias_dtype, Y,
+                             y_dtype, ldy, activation, &rows_max);
+  if (st) return st;
+  int num_cu = 0;
+  st = current_device(&num_cu);
+  if (st) return st;
+  const size_t need = lowbit_gemm_workspace_bytes(format, M, N, K);
+  if (need > LOWBIT_NOALLOC_SCRATCH_BYTES) return LOWBIT_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need) {
+    st = scratch_address(&ws);
+    if (st) return st;
+  }
+  const lowbit::GemmArgs a = make_args(format, K, ldx, W_packed, scales, N, bias, bias_dtype, y_dtype, ldy,
+                                       activation, ws);
   return run_problem(format, X, x_dtype, M, K, ldx, a, Y, y_dtype, ldy, rows_max, num_cu, force_variant(), stream);
 }
 

@@ -69,6 +69,8 @@ extern "C" {
 #define LOWBIT_ABI_VERSION 1
 #define LOWBIT_GROUP 128
 #define LOWBIT_MAX_GROUP 8   /* problems per lowbit_gemm_grouped call */
+/* Scratch that lowbit_gemm_noalloc keeps on each GPU: 16 MiB + 64 KiB. */
+#define LOWBIT_NOALLOC_SCRATCH_BYTES ((16u << 20) + (64u << 10))
 
 typedef enum {
   LOWBIT_OK = 0,
@@ -228,6 +230,26 @@ int32_t lowbit_gemm(int32_t format,
                     int32_t activation,
                     void* workspace, size_t workspace_bytes,
                     void* stream);
+
+/* lowbit_gemm with no workspace argument, for callers that cannot allocate
+ * device memory around a call: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. Same arguments (less workspace and
+ * workspace_bytes), same result bits and the same accuracy contract as
+ * lowbit_gemm. Where lowbit_gemm needs a workspace (M <= 16 with K split
+ * across workgroups), this entry point uses a scratch array of the library
+ * instead: LOWBIT_NOALLOC_SCRATCH_BYTES of device memory per GPU, held from
+ * the first call (or lowbit_init) on that GPU until the process ends. A
+ * problem that needs more than that returns LOWBIT_ERR_WORKSPACE. It calls
+ * no allocating routine. Every call on one GPU shares that GPU's scratch:
+ * calls that can overlap on one GPU (other streams, other host threads'
+ * streams) race on it and give wrong results; serialise them on one stream.
+ * Its counters start at zero and every call leaves them at zero. */
+int32_t lowbit_gemm_noalloc(int32_t format,
+                            const void* X, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx,
+                            const uint8_t* W_packed, const void* scales, int32_t group, int64_t N,
+                            const void* bias, int32_t bias_dtype,
+                            void* Y, int32_t y_dtype, int64_t ldy,
+                            int32_t activation, void* stream);
 
 /* Several independent linears of one shape in one launch: problem z computes
  *
