@@ -92,7 +92,7 @@ constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | ((n >> 4) << 14);
 }  // namespace large
 
 template <bool BF16, int FMT, int WN, int BMT = 128, int NST = 3>
-__global__ __launch_bounds__(64 * WN) void gemm_large_kernel(GemmArgs a, int tiles_m, int tiles_n) {
+__global__ __launch_bounds__(64 * WN) void gemm_large_kernel(GemmArgs a, int tiles_m, int tiles_n, int xcd_rows) {
   using namespace large;
   constexpr bool TERN = FMT == FMT_TERNARY;
   constexpr int BN = bn<WN>(), XR = BMT / (4 * WN);     // activation loads per wave and stage
@@ -107,12 +107,27 @@ __global__ __launch_bounds__(64 * WN) void gemm_large_kernel(GemmArgs a, int til
   const int lane = tid & 63, q = lane >> 5, r32 = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // XCD-aware tile order: consecutive workgroups land on different XCDs, so
-  // give each XCD a contiguous range of tiles (N fastest) to share L2.
-  int t = blockIdx.x;
-  const int T = tiles_m * tiles_n;
-  if ((T & 7) == 0) t = (t & 7) * (T >> 3) + (t >> 3);
-  const int m0 = (t / tiles_n) * BMT, n0 = (t % tiles_n) * BN;
+  // XCD-aware tile order: workgroup i runs on XCD i % 8 (round-robin
+  // dispatch), and each XCD gets one eighth of the tiles to share its L2
+  // (plan: xcd_order). xcd_rows = 0: a contiguous range of tiles, N fastest;
+  // xcd_rows = a > 0: the tile grid cut into a x (8 / a) equal blocks, block
+  // x for XCD x, row by row inside it (so the packed codes of a block's
+  // columns stay in the XCD's L2 while its rows stream through).
+  int tm_i, tn_i;
+  {
+    const int T = tiles_m * tiles_n;
+    const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+    if (xcd_rows > 0) {
+      const int b = 8 / xcd_rows, cols = tiles_n / b;
+      tm_i = (x / b) * (tiles_m / xcd_rows) + j / cols;
+      tn_i = (x % b) * cols + j % cols;
+    } else {
+      const int t = (T & 7) == 0 ? x * (T >> 3) + j : (int)blockIdx.x;
+      tm_i = t / tiles_n;
+      tn_i = t % tiles_n;
+    }
+  }
+  const int m0 = tm_i * BMT, n0 = tn_i * BN;
   const int G = a.K >> 7;
   const int64_t wrow = TERN ? (a.K >> 2) : (a.K >> 3);
   const float factor = code_factor<TERN>();
@@ -1017,20 +1032,57 @@ static bool large_pair(int M, int N, int num_cu, int variant) {
   return pair < 0.97 * wide;
 }
 
+// Which eighth of the tile grid each XCD takes (the kernel's xcd_rows): a
+// contiguous range (0) or a x (8 / a) equal blocks (a = 1, 2, 4, 8), the
+// one with the fewest bytes an XCD must fetch into its 4 MB L2, estimated
+// as its activation rows once plus its packed-code columns once if they fit
+// in about 2.5 MB, else once per tile row that a round of its concurrently
+// resident tiles starts (slots: workgroups resident on one XCD).
+static int xcd_order(int M, int N, int K, int fmt, int tm, int tn, int bmt, int bn, int slots) {
+  if ((tm * tn) % 8) return 0;
+  const double xrow = 2.0 * K * bmt;                                 // bytes of one tile row of X
+  const double wcol = (fmt == FMT_TERNARY ? K / 4.0 : K / 8.0) * bn + 2.0 * bn * (K / 128);
+  auto cost = [&](double rows, double cols, double conc_rows) {
+    const double w = cols * wcol;
+    const double refetch = w <= 2.5e6 ? 1.0 : std::max(1.0, rows / std::max(1.0, conc_rows));
+    return rows * xrow + w * refetch;
+  };
+  // contiguous ranges: T / 8 tiles, N fastest
+  const double per = (double)tm * tn / 8;
+  int best = 0;
+  double bc = cost(per / tn, std::min<double>(tn, per), (double)slots / tn);
+  for (int a = 1; a <= 8; a *= 2) {
+    const int b = 8 / a;
+    if (tm % a || tn % b) continue;
+    const double c = cost((double)tm / a, (double)tn / b, (double)slots / (tn / b));
+    if (c < 0.97 * bc) {
+      bc = c;
+      best = a;
+    }
+  }
+  (void)M;
+  (void)N;
+  return best;
+}
+
 template <bool BF16, int FMT>
 static void launch_large_t(const GemmArgs& a, int num_cu, int variant, hipStream_t st) {
+  const int xcd_cu = std::max(1, num_cu / 8);
   if (large_pair(a.M, a.N, num_cu, variant)) {
     const int tm = (a.M + 95) / 96, tn = (a.N + 255) / 256;
-    hipLaunchKernelGGL((gemm_large_kernel<BF16, FMT, 4, 96, 2>), dim3(tm * tn), dim3(256), 0, st, a, tm, tn);
+    const int xr = xcd_order(a.M, a.N, a.K, FMT, tm, tn, 96, 256, 2 * xcd_cu);
+    hipLaunchKernelGGL((gemm_large_kernel<BF16, FMT, 4, 96, 2>), dim3(tm * tn), dim3(256), 0, st, a, tm, tn, xr);
     return;
   }
   const int tm = (a.M + large::BM - 1) / large::BM;
   if (a.N >= 2048) {
     const int tn = (a.N + large::bn<8>() - 1) / large::bn<8>();
-    hipLaunchKernelGGL((gemm_large_kernel<BF16, FMT, 8>), dim3(tm * tn), dim3(512), 0, st, a, tm, tn);
+    const int xr = xcd_order(a.M, a.N, a.K, FMT, tm, tn, 128, 512, xcd_cu);
+    hipLaunchKernelGGL((gemm_large_kernel<BF16, FMT, 8>), dim3(tm * tn), dim3(512), 0, st, a, tm, tn, xr);
   } else {
     const int tn = (a.N + large::bn<4>() - 1) / large::bn<4>();
-    hipLaunchKernelGGL((gemm_large_kernel<BF16, FMT, 4>), dim3(tm * tn), dim3(256), 0, st, a, tm, tn);
+    const int xr = xcd_order(a.M, a.N, a.K, FMT, tm, tn, 128, 256, xcd_cu);
+    hipLaunchKernelGGL((gemm_large_kernel<BF16, FMT, 4>), dim3(tm * tn), dim3(256), 0, st, a, tm, tn, xr);
   }
 }
 
