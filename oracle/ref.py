@@ -337,6 +337,83 @@ def gelu(a: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# 4-bit group-quantised weights with a zero point (the text encoder's format)
+#
+# Page "Cómo Bonsai Ternary 4B revoluciona la difusión texto-imagen", section
+# "Arquitectura de despliegue y eficiencia en tiempo de ejecución": the
+# pipeline's text encoder runs compressed to 4-bit HQQ. The pages give no
+# layout. Reading taken here (parity of the HQQ layout itself is unpinned):
+# a weight is an unsigned 4-bit code q in 0..15 with an FP16 scale s and an
+# FP16 zero point z per group of 128 weights along K,
+#     w = s * (q - z),
+# and the packed row is a sequence of little-endian 32-bit words, word u
+# holding k = 8u .. 8u+7, the code of k = 8u + 2i + h (i in 0..3, h in {0, 1})
+# in bits [16h + 4i, 16h + 4i + 3] (even k in the low half word, odd k in the
+# high one, as the ternary layout).
+# ---------------------------------------------------------------------------
+
+def pack_int4(q: np.ndarray) -> np.ndarray:
+    """uint8 codes [N, K] in 0..15 -> uint8 [N, K/2] (4 bits per weight)."""
+    q = np.asarray(q)
+    N, K = q.shape
+    if K % 8:
+        raise ValueError("4-bit packing needs K % 8 == 0")
+    if (q < 0).any() or (q > 15).any():
+        raise ValueError("4-bit codes must lie in 0..15")
+    c = q.astype(np.uint32)
+    words = np.zeros((N, K // 8), dtype=np.uint32)
+    for j in range(8):                                       # position inside the word
+        i, h = divmod(j, 2)
+        words |= c[:, j::8] << np.uint32(16 * h + 4 * i)
+    return words.astype("<u4").view(np.uint8).reshape(N, K // 2)
+
+
+def unpack_int4(packed: np.ndarray, K: int) -> np.ndarray:
+    """uint8 [N, K/2] -> uint8 codes [N, K] (every 4-bit pattern is valid)."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    N = packed.shape[0]
+    words = packed.reshape(N, K // 2).view("<u4").astype(np.uint32)
+    q = np.zeros((N, K), dtype=np.uint8)
+    for j in range(8):
+        i, h = divmod(j, 2)
+        q[:, j::8] = ((words >> np.uint32(16 * h + 4 * i)) & np.uint32(15)).astype(np.uint8)
+    return q
+
+
+def dequantize_int4(q: np.ndarray, scales: np.ndarray, zeros: np.ndarray, group: int = GROUP) -> np.ndarray:
+    """W[n, k] = s[n, g] * (q[n, k] - z[n, g]), g = k // group, exactly in float64
+    (q - z is exact: z has an 11-bit significand and q < 16; the product of two
+    numbers of at most 11 and 16 significant bits is exact)."""
+    q = np.asarray(q)
+    N, K = q.shape
+    if K % group:
+        raise ValueError("K must be a multiple of the group size")
+    s = np.asarray(scales, dtype=np.float16).astype(np.float64)
+    z = np.asarray(zeros, dtype=np.float16).astype(np.float64)
+    if s.shape != (N, K // group) or z.shape != (N, K // group):
+        raise ValueError("scales and zeros must have shape [N, K/group]")
+    return np.repeat(s, group, axis=1) * (q.astype(np.float64) - np.repeat(z, group, axis=1))
+
+
+def linear_int4(x_bits: np.ndarray, x_dtype: str, q: np.ndarray, scales: np.ndarray, zeros: np.ndarray,
+                bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """A[m, n] = sum_k x[m, k] * s (q[n, k] - z) (+ bias[n]) in float64."""
+    A = decode(x_bits, x_dtype) @ dequantize_int4(q, scales, zeros).T
+    if bias is not None:
+        A = A + np.asarray(bias, dtype=np.float16).astype(np.float64)[None, :]
+    return A
+
+
+def magnitude_int4(x_bits: np.ndarray, x_dtype: str, q: np.ndarray, scales: np.ndarray, zeros: np.ndarray,
+                   bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """sum_k |x[m, k] * w[n, k]| (+ |bias[n]|)."""
+    Mg = np.abs(decode(x_bits, x_dtype)) @ np.abs(dequantize_int4(q, scales, zeros)).T
+    if bias is not None:
+        Mg = Mg + np.abs(np.asarray(bias, dtype=np.float16).astype(np.float64))[None, :]
+    return Mg
+
+
+# ---------------------------------------------------------------------------
 # Tolerance
 # ---------------------------------------------------------------------------
 

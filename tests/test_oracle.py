@@ -440,3 +440,81 @@ def test_check_detects_planted_errors():
     Ynan = Y.copy()
     Ynan[0, 0] = np.nan
     assert not oracle.check(Ynan, A, Mg, "bf16")[0]
+
+
+# ------------------------------------------------------- 4-bit with zero point ---
+
+def test_int4_pack_hand_literal(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "int4_pack_word.json")))
+    q = np.array([g["q"]], dtype=np.uint8)
+    assert oracle.pack_int4(q).tobytes().hex() == g["packed_hex"]
+
+
+def test_int4_every_code_at_every_position_by_byte_and_nibble():
+    """Byte B of a word holds the codes of two k in its two nibbles: with bit
+    position p = 16h + 4i for k = 2i + h, byte B = p // 8 and nibble (p % 8) // 4,
+    so the low nibble of byte B is k = 4 (B % 2) + B // 2 and the high nibble
+    k = 4 (B % 2) + 2 + B // 2. Every code value at every position."""
+    for v in range(16):
+        for j in range(8):
+            q = np.zeros((1, 8), dtype=np.uint8)
+            q[0, j] = v
+            b = oracle.pack_int4(q)[0]
+            for B in range(4):
+                lo_k, hi_k = 4 * (B % 2) + B // 2, 4 * (B % 2) + 2 + B // 2
+                assert b[B] & 15 == q[0, lo_k] and b[B] >> 4 == q[0, hi_k], (v, j, B)
+
+
+def test_int4_round_trip_and_rejects_out_of_range():
+    g = np.random.default_rng(7)
+    q = g.integers(0, 16, size=(5, 256), dtype=np.uint8)
+    p = oracle.pack_int4(q)
+    assert p.shape == (5, 128)
+    assert np.array_equal(oracle.unpack_int4(p, 256), q)
+    with pytest.raises(ValueError):
+        oracle.pack_int4(np.full((1, 8), 16, dtype=np.uint8))
+    with pytest.raises(ValueError):
+        oracle.pack_int4(np.zeros((1, 12), dtype=np.uint8))
+
+
+def test_int4_dequantize_closed_forms():
+    q = np.tile(np.arange(16, dtype=np.uint8), (3, 8))          # [3, 128]
+    # z = q's own integer value -> w = 0 where q == z; s = 1, z = 0 -> w = q
+    s1 = np.ones((3, 1), dtype=np.float16)
+    z0 = np.zeros((3, 1), dtype=np.float16)
+    assert np.array_equal(oracle.dequantize_int4(q, s1, z0), q.astype(np.float64))
+    z7 = np.full((3, 1), 7.0, dtype=np.float16)
+    W = oracle.dequantize_int4(q, s1, z7)
+    assert (W[q == 7] == 0).all() and W.min() == -7.0 and W.max() == 8.0
+    # a subnormal scale and a non-integer zero point stay exact
+    s_sub = np.full((3, 1), 2.0 ** -24, dtype=np.float16)
+    zf = np.full((3, 1), 7.5, dtype=np.float16)
+    W = oracle.dequantize_int4(q, s_sub, zf)
+    assert np.array_equal(W, (q.astype(np.float64) - 7.5) * 2.0 ** -24)
+
+
+def test_int4_worked_example(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "int4_worked_linear.json")))
+    k = np.arange(128)
+    q = np.stack([np.full(128, 5), k % 16]).astype(np.uint8)
+    x = np.stack([np.ones(128), np.where(k < 16, 2.0, 0.0)]).astype(np.float32)
+    xb = wl.to_bits(x, "bf16")
+    A = oracle.linear_int4(xb, "bf16", q, np.array(g["scales"], np.float16), np.array(g["zeros"], np.float16))
+    assert np.array_equal(A, np.array(g["Y"]))
+
+
+@pytest.mark.parametrize("K", [128, 256])
+def test_int4_linear_against_exact_rationals(K):
+    g = np.random.default_rng(K)
+    M, N = 3, 4
+    xb = wl.activations(np.random.Generator(np.random.PCG64(K)), M, K, "bf16")
+    q = g.integers(0, 16, size=(N, K), dtype=np.uint8)
+    s = (np.abs(g.standard_normal((N, K // 128))) * 0.01 + 1e-3).astype(np.float16)
+    z = (7.5 + g.standard_normal((N, K // 128))).astype(np.float16)
+    A = oracle.linear_int4(xb, "bf16", q, s, z)
+    X = oracle.decode(xb, "bf16")
+    for m in range(M):
+        for n in range(N):
+            exact = sum(Fraction(float(X[m, kk])) * Fraction(float(s[n, kk // 128])) *
+                        (Fraction(int(q[n, kk])) - Fraction(float(z[n, kk // 128]))) for kk in range(K))
+            assert abs(Fraction(A[m, n]) - exact) <= abs(exact) * Fraction(2) ** -45 + Fraction(2) ** -60
