@@ -21,12 +21,12 @@ LIB_PATH = os.path.join(HERE, "liblowbit.so")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_DTYPE, ERR_GROUP, ERR_WORKSPACE, ERR_DEVICE, ERR_HIP, ERR_OVERLAP = range(10)
 F16, BF16, F32, NONE = 0, 1, 2, 3
-BINARY, TERNARY, BASE3 = 1, 2, 3
+BINARY, TERNARY, BASE3, INT4 = 1, 2, 3, 4
 ACT_NONE, ACT_GELU = 0, 1
 GROUP = 128
 
-_FMT = {"ternary": TERNARY, "binary": BINARY, "base3": BASE3, TERNARY: TERNARY, BINARY: BINARY,
-        BASE3: BASE3}
+_FMT = {"ternary": TERNARY, "binary": BINARY, "base3": BASE3, "int4": INT4, TERNARY: TERNARY, BINARY: BINARY,
+        BASE3: BASE3, INT4: INT4}
 _DT = {torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
 _ACT = {None: ACT_NONE, "none": ACT_NONE, "gelu": ACT_GELU, ACT_NONE: ACT_NONE, ACT_GELU: ACT_GELU}
 
@@ -55,6 +55,10 @@ SIGNATURES = [
     ("lowbit_gemm_grouped_workspace_bytes", _SZ, [_I32, _I32, _I64, _I64, _I64]),
     ("lowbit_gemm_noalloc", _I32, [_I32, _P, _I32, _I64, _I64, _I64, _P, _P, _I32, _I64,
                                    _P, _I32, _P, _I32, _I64, _I32, _P]),
+    ("pack_int4", _I32, [_P, _I64, _I64, _P, _P, _P]),
+    ("lowbit_gemm_int4_workspace_bytes", _SZ, [_I64, _I64, _I64]),
+    ("lowbit_gemm_int4", _I32, [_P, _I32, _I64, _I64, _I64, _P, _P, _P, _I32, _I64,
+                                _P, _I32, _P, _I32, _I64, _I32, _P, _SZ, _P]),
 ]
 MAX_GROUP = 8
 
@@ -154,7 +158,9 @@ def _shared_workspace(device: torch.device, nbytes: int, stream) -> torch.Tensor
 
 
 def _row_bytes(fmt: int, K: int) -> int:
-    return (K + 4) // 5 if fmt == BASE3 else K // (4 if fmt == TERNARY else 8)
+    if fmt == BASE3:
+        return (K + 4) // 5
+    return K // {TERNARY: 4, BINARY: 8, INT4: 2}[fmt]
 
 
 def _counted(fn, src: torch.Tensor, N: int, K: int, out: torch.Tensor, check: bool, stream, what: str):
@@ -169,8 +175,9 @@ def _counted(fn, src: torch.Tensor, N: int, K: int, out: torch.Tensor, check: bo
 
 def _pack(fn, codes: torch.Tensor, fmt: int, check: bool, stream) -> torch.Tensor:
     _cuda(codes, "codes")
-    if codes.dtype != torch.int8 or codes.dim() != 2:
-        raise ValueError("codes must be a 2-D int8 tensor")
+    want = torch.uint8 if fmt == INT4 else torch.int8
+    if codes.dtype != want or codes.dim() != 2:
+        raise ValueError(f"codes must be a 2-D {want} tensor")
     codes = codes.contiguous()
     N, K = codes.shape
     out = torch.empty((N, _row_bytes(fmt, K)), dtype=torch.uint8, device=codes.device)
@@ -185,6 +192,54 @@ def pack_ternary(codes: torch.Tensor, check: bool = True, stream=None) -> torch.
 def pack_binary(codes: torch.Tensor, check: bool = True, stream=None) -> torch.Tensor:
     """int8 codes [N, K] in {-1,+1} -> packed uint8 [N, K/8] (K % 32 == 0)."""
     return _pack(lib().pack_binary, codes, BINARY, check, stream)
+
+
+def pack_int4(codes: torch.Tensor, check: bool = True, stream=None) -> torch.Tensor:
+    """uint8 codes [N, K] in 0..15 -> packed uint8 [N, K/2] (K % 8 == 0)."""
+    return _pack(lib().pack_int4, codes, INT4, check, stream)
+
+
+def gemm_int4(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor,
+              bias: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None, activation=None,
+              out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+              stream=None) -> torch.Tensor:
+    """Y = act(X W^T + bias) with W = s * (q - z) from 4-bit codes (lowbit_gemm_int4).
+
+    x: [M, K] fp16/bf16; packed: [N, K/2] uint8; scales, zeros: fp16 [N, K/128].
+    A workspace for the row sums is allocated per call unless one is given."""
+    for t, nm in ((x, "x"), (packed, "packed"), (scales, "scales"), (zeros, "zeros")):
+        _cuda(t, nm)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit stride along K")
+    M, K = x.shape
+    N = packed.shape[0]
+    packed, scales, zeros = packed.contiguous(), scales.contiguous(), zeros.contiguous()
+    _check_packed(INT4, packed, N, K)
+    for t, nm in ((scales, "scales"), (zeros, "zeros")):
+        if t.dtype != torch.float16 or tuple(t.shape) != (N, K // GROUP):
+            raise ValueError(f"{nm} must be float16 [{N}, {K // GROUP}]")
+    if bias is not None:
+        _cuda(bias, "bias")
+        bias = bias.contiguous()
+        if bias.numel() != N or bias.dtype not in _DT:
+            raise ValueError(f"bias must hold {N} float16, bfloat16 or float32 values")
+    odt = out_dtype or x.dtype
+    if out is None:
+        out = torch.empty((M, N), dtype=odt, device=x.device)
+    elif tuple(out.shape) != (M, N) or out.stride(1) != 1 or out.dtype not in _DT:
+        raise ValueError(f"out must be [{M}, {N}] with unit stride along N")
+    need = int(lib().lowbit_gemm_int4_workspace_bytes(M, N, K))
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    elif workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, "
+                         f"lowbit_gemm_int4 needs {need}")
+    _check(lib().lowbit_gemm_int4(
+        x.data_ptr(), _DT[x.dtype], M, K, x.stride(0), packed.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
+        GROUP, N, _ptr(bias), NONE if bias is None else _DT[bias.dtype], out.data_ptr(), _DT[out.dtype],
+        out.stride(0), _ACT[activation], workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+        _stream(stream)), "lowbit_gemm_int4")
+    return out
 
 
 def pack_base3(codes: torch.Tensor, check: bool = True, stream=None) -> torch.Tensor:
@@ -218,12 +273,13 @@ def _check_packed(fmt, packed: torch.Tensor, N: int, K: int):
 
 
 def unpack(fmt, packed: torch.Tensor, K: int, stream=None) -> Tuple[torch.Tensor, int]:
-    """packed [N, K/4, K/8 or ceil(K/5)] -> (int8 codes [N, K], number of invalid codes)."""
+    """packed [N, K/4, K/8, ceil(K/5) or K/2] -> (codes [N, K], number of invalid codes);
+    int8 codes, uint8 for the 4-bit format."""
     _cuda(packed, "packed")
     packed = packed.contiguous()
     N = packed.shape[0]
     _check_packed(fmt, packed, N, K)
-    codes = torch.empty((N, K), dtype=torch.int8, device=packed.device)
+    codes = torch.empty((N, K), dtype=torch.uint8 if _FMT[fmt] == INT4 else torch.int8, device=packed.device)
     cnt = torch.empty(1, dtype=torch.int32, device=packed.device)
     _check(lib().unpack_lowbit(_FMT[fmt], packed.data_ptr(), N, K, codes.data_ptr(), cnt.data_ptr(),
                                _stream(stream)), "unpack_lowbit")

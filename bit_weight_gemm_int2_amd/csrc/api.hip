@@ -22,6 +22,8 @@ hipError_t launch_base3_to_int2(const uint8_t* base3, int64_t N, int64_t K, uint
 hipError_t launch_gemm(int fmt, bool x_bf16, GemmArgs a, int num_cu, int variant, hipStream_t st,
                        const GemmGroup* group = nullptr, int count = 1);
 hipError_t launch_gelu(const void* in, void* out, int dtype, int64_t count, hipStream_t st);
+hipError_t launch_gemm_int4(bool x_bf16, GemmArgs a, int num_cu, hipStream_t st);
+int64_t int4_rows(int64_t M);
 size_t small_workspace_bytes(int M, int N, int K, int num_cu, int variant, int count = 1);
 bool small_path(int M, int N, int K, int variant, int count = 1);
 }  // namespace lowbit
@@ -169,6 +171,7 @@ int64_t lowbit_packed_bytes(int32_t format, int64_t N, int64_t K) {
   if (format == LOWBIT_TERNARY_INT2) return K % 16 ? -1 : N * (K / 4);
   if (format == LOWBIT_BINARY_1BIT) return K % 32 ? -1 : N * (K / 8);
   if (format == LOWBIT_TERNARY_BASE3) return N * ((K + 4) / 5);
+  if (format == LOWBIT_INT4_ZP) return K % 8 ? -1 : N * (K / 2);
   return -1;
 }
 
@@ -180,6 +183,7 @@ int64_t lowbit_scale_count(int64_t N, int64_t K, int32_t group) {
 static int kernel_format(int32_t format) {
   return format == LOWBIT_TERNARY_INT2 ? lowbit::FMT_TERNARY
        : format == LOWBIT_BINARY_1BIT  ? lowbit::FMT_BINARY
+       : format == LOWBIT_INT4_ZP      ? lowbit::FMT_INT4
                                        : lowbit::FMT_BASE3;
 }
 
@@ -215,9 +219,15 @@ int32_t pack_base3(const int8_t* codes, int64_t N, int64_t K, uint8_t* packed,
   return pack_common(LOWBIT_TERNARY_BASE3, codes, N, K, packed, invalid_count, stream);
 }
 
+int32_t pack_int4(const uint8_t* codes, int64_t N, int64_t K, uint8_t* packed, int32_t* invalid_count,
+                  void* stream) {
+  return pack_common(LOWBIT_INT4_ZP, (const int8_t*)codes, N, K, packed, invalid_count, stream);
+}
+
 int32_t unpack_lowbit(int32_t format, const uint8_t* packed, int64_t N, int64_t K, int8_t* codes,
                       int32_t* invalid_count, void* stream) {
-  if (format != LOWBIT_TERNARY_INT2 && format != LOWBIT_BINARY_1BIT && format != LOWBIT_TERNARY_BASE3)
+  if (format != LOWBIT_TERNARY_INT2 && format != LOWBIT_BINARY_1BIT && format != LOWBIT_TERNARY_BASE3 &&
+      format != LOWBIT_INT4_ZP)
     return LOWBIT_ERR_DTYPE;
   if (!codes || !packed) return LOWBIT_ERR_NULL;
   if (lowbit_packed_bytes(format, N, K) < 0) return LOWBIT_ERR_SHAPE;
@@ -489,6 +499,47 @@ int32_t lowbit_gemm_grouped(int32_t count, int32_t format, const void* const* X,
   a.M = (int)M;
   hipError_t e = lowbit::launch_gemm(format == LOWBIT_TERNARY_INT2 ? lowbit::FMT_TERNARY : lowbit::FMT_BINARY,
                                      x_dtype == LOWBIT_BF16, a, num_cu, variant, (hipStream_t)stream, &g, count);
+  return e == hipSuccess ? LOWBIT_OK : LOWBIT_ERR_HIP;
+}
+
+size_t lowbit_gemm_int4_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || N < 1 || K < 128 || K % 128 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return 0;
+  return (size_t)(K / 128) * (size_t)lowbit::int4_rows(M) * sizeof(float);
+}
+
+int32_t lowbit_gemm_int4(const void* X, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx, const uint8_t* W_packed,
+                         const void* scales, const void* zeros, int32_t group, int64_t N, const void* bias,
+                         int32_t bias_dtype, void* Y, int32_t y_dtype, int64_t ldy, int32_t activation,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  // every check of lowbit_gemm (its packed-size rules read for K/2 bytes a row)
+  if (!zeros) return LOWBIT_ERR_NULL;
+  int64_t rows_max = 0;
+  int32_t st = check_problem(LOWBIT_TERNARY_INT2, X, x_dtype, M, K, ldx, W_packed, scales, group, N, bias,
+                             bias_dtype, Y, y_dtype, ldy, activation, &rows_max);
+  if (st) return st;
+  if (N * (K / 2) > kOffsetSpan || M > rows_max) return LOWBIT_ERR_SHAPE;
+  if (!aligned(zeros, 2)) return LOWBIT_ERR_ALIGN;
+  const int64_t yb = y_span(M, N, ldy, y_dtype), sb = N * (K / 128) * 2;
+  if (overlaps(Y, yb, W_packed, N * (K / 2)) || overlaps(Y, yb, zeros, sb)) return LOWBIT_ERR_OVERLAP;
+  const size_t need = lowbit_gemm_int4_workspace_bytes(M, N, K);
+  if (!workspace || workspace_bytes < need) return LOWBIT_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return LOWBIT_ERR_ALIGN;
+  const int64_t wn = (int64_t)workspace_bytes;
+  if (overlaps(workspace, wn, Y, yb) || overlaps(workspace, wn, X, ((M - 1) * ldx + K) * 2) ||
+      overlaps(workspace, wn, W_packed, N * (K / 2)) || overlaps(workspace, wn, scales, sb) ||
+      overlaps(workspace, wn, zeros, sb) || overlaps(workspace, wn, bias, N * (bias_dtype == LOWBIT_F32 ? 4 : 2)))
+    return LOWBIT_ERR_OVERLAP;
+  int num_cu = 0;
+  st = current_device(&num_cu);
+  if (st) return st;
+  lowbit::GemmArgs a = make_args(LOWBIT_INT4_ZP, K, ldx, W_packed, scales, N, bias, bias_dtype, y_dtype, ldy,
+                                 activation, workspace);
+  a.X = (const uint16_t*)X;
+  a.Y = Y;
+  a.M = (int)M;
+  a.Z = (const uint16_t*)zeros;
+  a.ldr = lowbit::int4_rows(M);
+  hipError_t e = lowbit::launch_gemm_int4(x_dtype == LOWBIT_BF16, a, num_cu, (hipStream_t)stream);
   return e == hipSuccess ? LOWBIT_OK : LOWBIT_ERR_HIP;
 }
 

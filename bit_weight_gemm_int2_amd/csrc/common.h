@@ -14,7 +14,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 enum { DT_F16 = 0, DT_BF16 = 1, DT_F32 = 2, DT_NONE = 3 };
-enum { FMT_BINARY = 1, FMT_TERNARY = 2, FMT_BASE3 = 3 };
+enum { FMT_BINARY = 1, FMT_TERNARY = 2, FMT_BASE3 = 3, FMT_INT4 = 4 };
 enum { ACT_NONE = 0, ACT_GELU = 1 };
 
 struct GemmArgs {
@@ -29,7 +29,9 @@ struct GemmArgs {
   int y_dtype;
   int act;
   int M, N, K;
-  float* ws;           // caller workspace (no kernel uses one at present)
+  float* ws;           // caller workspace: split-K partials (small M) or the 4-bit row sums
+  const uint16_t* Z;   // fp16 zero points [N][K/128] (4-bit format only)
+  int64_t ldr;         // row stride of the 4-bit row sums [K/128][ldr]
 };
 
 // The operands of the problems of one grouped launch: same shapes, types and
@@ -178,6 +180,28 @@ __device__ __forceinline__ u32x4 bin_chunk(uint32_t w, int c, uint32_t sign, uin
   for (int v = 0; v < 4; ++v) r[v] = (rotr(w, 17 + 4 * c + v) & sign) | two;
   return r;
 }
+
+// Eight consecutive k of a 4-bit word (k = 2v and 2v + 1 at bits 4v and
+// 16 + 4v) as the MFMA values 128 + q, exact in both 16-bit types: in BF16
+// the values 128 .. 143 are 0x4300 | q (exponent of 128, q in the seven
+// mantissa bits), in FP16 they are 0x5800 | q << 3 (mantissa spacing 1/8 of
+// the ten bits, so q sits three bits up). One shift and one AND-OR per
+// register; zero mask and base give an all-zero operand.
+template <bool BF16>
+__device__ __forceinline__ u32x4 int4_chunk(uint32_t w, uint32_t mask, uint32_t base) {
+  u32x4 r;
+  if constexpr (BF16) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) r[v] = ((w >> (4 * v)) & mask) | base;
+  } else {
+    r[0] = ((w << 3) & mask) | base;
+#pragma unroll
+    for (int v = 1; v < 4; ++v) r[v] = ((w >> (4 * v - 3)) & mask) | base;
+  }
+  return r;
+}
+template <bool BF16> __device__ __forceinline__ constexpr uint32_t int4_mask() { return BF16 ? 0x000F000Fu : 0x00780078u; }
+template <bool BF16> __device__ __forceinline__ constexpr uint32_t int4_base() { return BF16 ? 0x43004300u : 0x58005800u; }
 
 // Factor that turns an MFMA sum of the fed values back into sum x * t.
 template <bool TERN>

@@ -80,13 +80,22 @@ constexpr int BM = 128;
 constexpr int ROW_BYTES = 256;                 // 128 k x 2 bytes
 template <int BMT> constexpr int x_bytes() { return BMT * ROW_BYTES; }   // activations per stage
 template <int WN> constexpr int bn() { return 64 * WN; }
-template <int WN> constexpr int w_bytes() { return bn<WN>() * 32; }   // packed codes (ternary size)
+// LDS bytes of packed codes per column and group (binary uses 16 of its 32)
+template <int FMT> constexpr int code_bytes() { return FMT == FMT_INT4 ? 64 : 32; }
+template <int FMT, int WN> constexpr int w_bytes() { return bn<WN>() * code_bytes<FMT>(); }
 template <int WN> constexpr int s_bytes() { return bn<WN>() * 4; }    // scales, 4-byte slots
-template <int WN, int BMT> constexpr int stage_bytes() { return x_bytes<BMT>() + w_bytes<WN>() + s_bytes<WN>(); }
+// a stage: activations, codes, scales, and for the 4-bit format the zero
+// points (4-byte slots) and the tile rows' activation sums of the group
+template <int FMT, int WN, int BMT> constexpr int stage_bytes() {
+  return x_bytes<BMT>() + w_bytes<FMT, WN>() + s_bytes<WN>() + (FMT == FMT_INT4 ? s_bytes<WN>() + BMT * 4 : 0);
+}
 // DMA loads per wave and stage: activations (BMT rows, 4 per load, split
-// over the waves) + codes (2 ternary, 1 binary) + scales (1)
-template <bool TERN, int WN, int BMT>
-constexpr int stage_loads() { return BMT / (4 * WN) + (TERN ? 2 : 1) + 1; }
+// over the waves) + codes (2 ternary, 1 binary, 4 for 4-bit) + scales (1)
+// (+ zero points and row sums for 4-bit)
+template <int FMT, int WN, int BMT>
+constexpr int stage_loads() {
+  return BMT / (4 * WN) + (FMT == FMT_TERNARY ? 2 : FMT == FMT_INT4 ? 4 : 1) + 1 + (FMT == FMT_INT4 ? 2 : 0);
+}
 // s_waitcnt immediate for vmcnt(n), expcnt(7), lgkmcnt(0)
 constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | ((n >> 4) << 14); }
 }  // namespace large
@@ -94,10 +103,13 @@ constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | ((n >> 4) << 14);
 template <bool BF16, int FMT, int WN, int BMT = 128, int NST = 3>
 __global__ __launch_bounds__(64 * WN) void gemm_large_kernel(GemmArgs a, int tiles_m, int tiles_n, int xcd_rows) {
   using namespace large;
-  constexpr bool TERN = FMT == FMT_TERNARY;
+  constexpr bool TERN = FMT == FMT_TERNARY, I4 = FMT == FMT_INT4;
   constexpr int BN = bn<WN>(), XR = BMT / (4 * WN);     // activation loads per wave and stage
   constexpr int IB = BMT / 32;                          // 32-row blocks per wave
-  constexpr int X_BYTES = x_bytes<BMT>(), W_BYTES = w_bytes<WN>(), STAGE_BYTES = stage_bytes<WN, BMT>();
+  constexpr int CB = code_bytes<FMT>();
+  constexpr int X_BYTES = x_bytes<BMT>(), W_BYTES = w_bytes<FMT, WN>(), STAGE_BYTES = stage_bytes<FMT, WN, BMT>();
+  constexpr int RW = BMT / WN;                          // 4-bit: row sums each wave copies per stage
+  static_assert(!I4 || (NST == 2 && RW % 4 == 0), "4-bit: two stages, row sums in 16-byte loads");
   static_assert(NST == 2 || NST == 3, "two or three stages");
   static_assert(BMT % (4 * WN) == 0 && BMT % 32 == 0, "tile height");
   static_assert(WN * BMT * 128 <= NST * STAGE_BYTES, "epilogue staging fits in the stages");
@@ -129,8 +141,8 @@ __global__ __launch_bounds__(64 * WN) void gemm_large_kernel(GemmArgs a, int til
   }
   const int m0 = tm_i * BMT, n0 = tn_i * BN;
   const int G = a.K >> 7;
-  const int64_t wrow = TERN ? (a.K >> 2) : (a.K >> 3);
-  const float factor = code_factor<TERN>();
+  const int64_t wrow = I4 ? (a.K >> 1) : TERN ? (a.K >> 2) : (a.K >> 3);
+  const float factor = I4 ? 1.0f : code_factor<TERN>();
   const int wcol0 = n0 + 64 * wave;                     // first column of this wave
 
   // ---- stage g -> LDS buffer `buf` (DMA only) ----
@@ -145,8 +157,16 @@ __global__ __launch_bounds__(64 * WN) void gemm_large_kernel(GemmArgs a, int til
     const int m = min(m0 + r, a.M - 1);                 // rows past M: any valid row
     xoff[it] = (uint32_t)(((int64_t)m * a.ldx + 8 * c) * 2);
   }
-  uint32_t woff[2], soff;
-  if (TERN) {
+  uint32_t woff[I4 ? 4 : 2], soff;
+  if (I4) {
+    // 64 bytes per column: LDS slot h of local column c holds 16-byte chunk
+    // h ^ ((c >> 2) & 3), which keeps the fragment reads bank-conflict free
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int c = 16 * it + (lane >> 2);
+      woff[it] = (uint32_t)(min(wcol0 + c, a.N - 1) * wrow + 16 * ((lane & 3) ^ ((c >> 2) & 3)));
+    }
+  } else if (TERN) {
     // LDS slot h of local column c holds 16-byte half h ^ bit 3 of c, so the
     // fragment reads (16 consecutive columns, same half) hit distinct banks
 #pragma unroll
@@ -164,12 +184,24 @@ __global__ __launch_bounds__(64 * WN) void gemm_large_kernel(GemmArgs a, int til
 #pragma unroll
     for (int it = 0; it < XR; ++it)
       dma_lds16(xg, xoff[it], lds_addr(base + (4 * XR * wave + 4 * it) * ROW_BYTES));
-    uint8_t* wb = base + X_BYTES + wave * (64 * 32);
-    const uint8_t* wg = a.W + g * (TERN ? 32 : 16);
+    uint8_t* wb = base + X_BYTES + wave * (64 * CB);
+    const uint8_t* wg = a.W + g * (I4 ? 64 : TERN ? 32 : 16);
     dma_lds16(wg, woff[0], lds_addr(wb));
-    if (TERN) dma_lds16(wg, woff[1], lds_addr(wb + 1024));
+    if (TERN || I4) dma_lds16(wg, woff[1], lds_addr(wb + 1024));
+    if (I4) {
+      dma_lds16(wg, woff[2], lds_addr(wb + 2048));
+      dma_lds16(wg, woff[3], lds_addr(wb + 3072));
+    }
     // scales: lane l -> 4-byte slot l (2-byte load, zero-extended)
     dma_lds2((const uint8_t*)a.S + 2 * g, soff, lds_addr(base + X_BYTES + W_BYTES + wave * 256));
+    if (I4) {
+      // zero points likewise, then this wave's RW rows of the group's row
+      // sums (row-sum array padded past M, so every row read exists)
+      dma_lds2((const uint8_t*)a.Z + 2 * g, soff, lds_addr(base + X_BYTES + W_BYTES + BN * 4 + wave * 256));
+      const float* rg = a.ws + g * a.ldr + m0 + RW * wave;
+      if (lane < RW / 4)
+        dma_lds16(rg, 16 * lane, lds_addr(base + X_BYTES + W_BYTES + 2 * BN * 4 + 4 * RW * wave));
+    }
   };
 
   auto afrag = [&](const uint8_t* xb, int i, int s) -> u32x4 {
@@ -191,22 +223,27 @@ __global__ __launch_bounds__(64 * WN) void gemm_large_kernel(GemmArgs a, int til
   for (int g = 0; g < G; ++g) {
     // stage g complete (three stages: only this wave's stage g+1 loads may
     // be in flight), and every wave's part of it visible
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(NST == 3 ? stage_loads<TERN, WN, BMT>() : 0));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(NST == 3 ? stage_loads<FMT, WN, BMT>() : 0));
     __syncthreads();
     // past the end this copies the last group into a buffer nobody reads
     if (NST == 3) stage(min(g + 2, G - 1), buf == 0 ? 2 : buf - 1);
     else stage(min(g + 1, G - 1), buf ^ 1);
     const uint8_t* xb = smem[buf];
-    const uint8_t* wb = smem[buf] + X_BYTES + wave * (64 * 32);
+    const uint8_t* wb = smem[buf] + X_BYTES + wave * (64 * CB);
     const uint8_t* sbuf = smem[buf] + X_BYTES + W_BYTES + wave * 256;
 
     // codes, scale and Horner rescale of each column block
-    u32x4 bw[2];
+    u32x4 bw[2], bw2[2];
     uint32_t tm[2], mk[2], bs[2];
+    float zc[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int col = 32 * j + r32;
-      if (TERN) {
+      if (I4) {
+        const int sw = (col >> 2) & 3;
+        bw[j] = *(const u32x4*)(wb + col * 64 + 16 * ((2 * q) ^ sw));
+        bw2[j] = *(const u32x4*)(wb + col * 64 + 16 * ((2 * q + 1) ^ sw));
+      } else if (TERN) {
         bw[j] = *(const u32x4*)(wb + col * 32 + 16 * (q ^ ((col >> 3) & 1)));
       } else {
         const u32x2 v = *(const u32x2*)(wb + col * 16 + 8 * q);
@@ -219,9 +256,13 @@ __global__ __launch_bounds__(64 * WN) void gemm_large_kernel(GemmArgs a, int til
       // rounding-size term per group, far inside the accuracy bound
       const float r = zero ? 1.0f : cref[j] * __builtin_amdgcn_rcpf(sc);
       cref[j] = zero ? cref[j] : sc;
-      tm[j] = zero ? 0u : TERN_MASK;
+      tm[j] = zero ? 0u : I4 ? int4_mask<BF16>() : TERN_MASK;
       mk[j] = zero ? 0u : BIN_SIGN;
-      bs[j] = zero ? 0u : BIN_TWO;
+      bs[j] = zero ? 0u : I4 ? int4_base<BF16>() : BIN_TWO;
+      if (I4) {
+        // the MFMAs add sum x (128 + q); (128 + z) times the row sum comes off
+        zc[j] = zero ? 0.0f : 128.0f + half_bits_to_float((uint16_t)*(const uint32_t*)(sbuf + BN * 4 + col * 4));
+      }
 #pragma unroll
       for (int i = 0; i < IB; ++i) acc[i][j] *= r;
     }
@@ -238,11 +279,29 @@ __global__ __launch_bounds__(64 * WN) void gemm_large_kernel(GemmArgs a, int til
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const u32x4 bf = TERN ? tern_chunk(bw[j][st >> 1], st & 1, tm[j])
-                              : bin_chunk(bw[j][st >> 2], st & 3, mk[j], bs[j]);
+        u32x4 bf;
+        if constexpr (I4) bf = int4_chunk<BF16>(st < 4 ? bw[j][st] : bw2[j][st - 4], tm[j], bs[j]);
+        else if constexpr (TERN) bf = tern_chunk(bw[j][st >> 1], st & 1, tm[j]);
+        else bf = bin_chunk(bw[j][st >> 2], st & 3, mk[j], bs[j]);
 #pragma unroll
         for (int i = 0; i < IB; ++i) acc[i][j] = mfma32<BF16>(A[st & 1][i], bf, acc[i][j]);
       }
+    }
+    if constexpr (I4) {
+      // acc -= (128 + z) * (sum of the group's activations) per row, in the
+      // group's scale units; lane rows 32 i + 8 e4 + 4 q + (0..3)
+      const float* rs = (const float*)(smem[buf] + X_BYTES + W_BYTES + 2 * BN * 4);
+#pragma unroll
+      for (int i = 0; i < IB; ++i)
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const f32x4 rv = *(const f32x4*)(rs + 32 * i + 8 * e4 + 4 * q);
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              acc[i][j][4 * e4 + e] = __builtin_fmaf(-zc[j], rv[e], acc[i][j][4 * e4 + e]);
+        }
     }
     buf = NST == 3 ? (buf == 2 ? 0 : buf + 1) : buf ^ 1;
   }
@@ -843,6 +902,39 @@ __global__ void gelu_kernel(const void* in, void* out, int dtype, int64_t count)
   }
 }
 
+// Row sums of the activations per 128-group for the 4-bit format:
+// R[g][m] = sum_{k in group g} x[m][k] in FP32, rows m >= M up to the padded
+// row count written as zeros. One thread per (group, row); sixteen sums of
+// eight consecutive values, then a pairwise tree over the sixteen (at most
+// 11 roundings on the way to any one result).
+__global__ void rowsum_kernel(const uint16_t* X, int64_t ldx, int M, int G, int64_t ldr, float* R, int bf16) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < (int64_t)G * ldr;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int g = (int)(i / ldr);
+    const int64_t m = i - (int64_t)g * ldr;
+    float c16[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) c16[c] = 0.0f;
+    if (m < M) {
+      const uint16_t* x = X + m * ldx + ((int64_t)g << 7);
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        const u32x4 v = *(const u32x4*)(x + 8 * c);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint16_t h = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+          c16[c] += bf16 ? bf16_bits_to_float(h) : half_bits_to_float(h);
+        }
+      }
+    }
+#pragma unroll
+    for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+      for (int c = 0; c < w; ++c) c16[c] += c16[c + w];
+    R[(int64_t)g * ldr + m] = c16[0];
+  }
+}
+
 // ===========================================================================
 // Host-side launch helpers
 // ===========================================================================
@@ -1041,7 +1133,8 @@ static bool large_pair(int M, int N, int num_cu, int variant) {
 static int xcd_order(int M, int N, int K, int fmt, int tm, int tn, int bmt, int bn, int slots) {
   if ((tm * tn) % 8) return 0;
   const double xrow = 2.0 * K * bmt;                                 // bytes of one tile row of X
-  const double wcol = (fmt == FMT_TERNARY ? K / 4.0 : K / 8.0) * bn + 2.0 * bn * (K / 128);
+  const double wcol = (fmt == FMT_INT4 ? K / 2.0 : fmt == FMT_TERNARY ? K / 4.0 : K / 8.0) * bn +
+                      (fmt == FMT_INT4 ? 4.0 : 2.0) * bn * (K / 128);
   auto cost = [&](double rows, double cols, double conc_rows) {
     const double w = cols * wcol;
     const double refetch = w <= 2.5e6 ? 1.0 : std::max(1.0, rows / std::max(1.0, conc_rows));
@@ -1138,6 +1231,33 @@ hipError_t launch_gemm(int fmt, bool x_bf16, GemmArgs a, int num_cu, int variant
         else launch_large_t<false, FMT_BINARY>(a, num_cu, variant, st);
       }
     }
+  }
+  return hipGetLastError();
+}
+
+// Padded row count of the 4-bit row sums: every tile row the kernel reads.
+int64_t int4_rows(int64_t M) { return (M + 127) / 128 * 128 + 128; }
+
+// 4-bit GEMM (any M): the row sums, then the large-M kernel with two stages
+// (a.ws: the row sums, a.ldr: int4_rows(M)).
+hipError_t launch_gemm_int4(bool x_bf16, GemmArgs a, int num_cu, hipStream_t st) {
+  const int G = a.K >> 7;
+  const int64_t work = (int64_t)G * a.ldr;
+  const int64_t blocks = std::min<int64_t>((work + 255) / 256, 65535);
+  hipLaunchKernelGGL(rowsum_kernel, dim3((unsigned)blocks), dim3(256), 0, st, a.X, a.ldx, a.M, G, a.ldr, a.ws,
+                     x_bf16 ? 1 : 0);
+  const int tm = (a.M + large::BM - 1) / large::BM;
+  const int xcd_cu = std::max(1, num_cu / 8);
+  if (a.N >= 2048) {
+    const int tn = (a.N + large::bn<8>() - 1) / large::bn<8>();
+    const int xr = xcd_order(a.M, a.N, a.K, FMT_INT4, tm, tn, 128, 512, xcd_cu);
+    if (x_bf16) hipLaunchKernelGGL((gemm_large_kernel<true, FMT_INT4, 8, 128, 2>), dim3(tm * tn), dim3(512), 0, st, a, tm, tn, xr);
+    else hipLaunchKernelGGL((gemm_large_kernel<false, FMT_INT4, 8, 128, 2>), dim3(tm * tn), dim3(512), 0, st, a, tm, tn, xr);
+  } else {
+    const int tn = (a.N + large::bn<4>() - 1) / large::bn<4>();
+    const int xr = xcd_order(a.M, a.N, a.K, FMT_INT4, tm, tn, 128, 256, xcd_cu);
+    if (x_bf16) hipLaunchKernelGGL((gemm_large_kernel<true, FMT_INT4, 4, 128, 2>), dim3(tm * tn), dim3(256), 0, st, a, tm, tn, xr);
+    else hipLaunchKernelGGL((gemm_large_kernel<false, FMT_INT4, 4, 128, 2>), dim3(tm * tn), dim3(256), 0, st, a, tm, tn, xr);
   }
   return hipGetLastError();
 }

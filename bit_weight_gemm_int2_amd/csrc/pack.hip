@@ -111,6 +111,38 @@ __global__ void unpack_binary_kernel(const uint32_t* __restrict__ in, int8_t* __
   }
 }
 
+// 4-bit codes (the text encoder's group-quantised weights, lowbit.h): uint8
+// codes 0 .. 15, eight per word, the code of k = 2i + h at bits 16h + 4i.
+// Codes above 15 are counted and stored as 0.
+__global__ void pack_int4_kernel(const uint8_t* __restrict__ codes, uint32_t* __restrict__ out, int64_t nwords,
+                                 int32_t* counter) {
+  int bad = 0;
+  for (int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; w < nwords;
+       w += (int64_t)gridDim.x * blockDim.x) {
+    const u32x2 v = *(const u32x2*)(codes + 8 * w);
+    uint32_t r = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t q = (v[j >> 2] >> (8 * (j & 3))) & 0xFFu;
+      bad += q > 15u ? 1 : 0;
+      r |= (q > 15u ? 0u : q) << (16 * (j & 1) + 4 * (j >> 1));
+    }
+    out[w] = r;
+  }
+  if (counter) count_invalid(counter, bad);
+}
+
+__global__ void unpack_int4_kernel(const uint32_t* __restrict__ in, uint8_t* __restrict__ codes, int64_t nwords) {
+  for (int64_t w = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; w < nwords;
+       w += (int64_t)gridDim.x * blockDim.x) {
+    const uint32_t x = in[w];
+    u32x2 o = {0u, 0u};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j >> 2] |= ((x >> (16 * (j & 1) + 4 * (j >> 1))) & 15u) << (8 * (j & 3));
+    *(u32x2*)(codes + 8 * w) = o;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Base-3 storage: five ternary values per byte (3^5 = 243 <= 256), the form
 // that approaches the log2(3) bits the pages price a ternary value at
@@ -374,6 +406,12 @@ hipError_t launch_pack(int fmt, const int8_t* codes, int64_t N, int64_t K, uint8
                        codes, packed, N, K, counter);
     return hipGetLastError();
   }
+  if (fmt == FMT_INT4) {
+    const int64_t nwords = N * K / 8;
+    hipLaunchKernelGGL(pack_int4_kernel, dim3(grid_for(nwords, 256)), dim3(256), 0, st, (const uint8_t*)codes,
+                       (uint32_t*)packed, nwords, counter);
+    return hipGetLastError();
+  }
   int64_t nwords = N * K / (fmt == FMT_TERNARY ? 16 : 32);
   const int block = 256;
   if (fmt == FMT_TERNARY)
@@ -391,6 +429,12 @@ hipError_t launch_unpack(int fmt, const uint8_t* packed, int64_t N, int64_t K, i
   if (fmt == FMT_BASE3) {
     hipLaunchKernelGGL(unpack_base3_kernel, dim3(grid_for_rows(N, (K + 4) / 5)), dim3(256), 0, st,
                        packed, codes, N, K, counter);
+    return hipGetLastError();
+  }
+  if (fmt == FMT_INT4) {
+    const int64_t nwords = N * K / 8;
+    hipLaunchKernelGGL(unpack_int4_kernel, dim3(grid_for(nwords, 256)), dim3(256), 0, st, (const uint32_t*)packed,
+                       (uint8_t*)codes, nwords);
     return hipGetLastError();
   }
   int64_t nwords = N * K / (fmt == FMT_TERNARY ? 16 : 32);

@@ -52,6 +52,11 @@
  *    byte of a row holds the K mod 5 leftover values when K mod 5 != 0. Bytes
  *    243 .. 255 are invalid. 1.6 bits per value, the nearest byte-aligned rate
  *    to the log2(3) ~ 1.585 bits the pages price a ternary value at.
+ *  4-bit with a zero point (the text encoder's format; lowbit_gemm_int4):
+ *    an unsigned code q in 0..15 per weight, w = s * (q - z) with an FP16
+ *    scale s and an FP16 zero point z per group of 128 along K. Word u of a
+ *    row holds k = 8u .. 8u+7; the code of k = 8u + 2i + h (i = 0..3,
+ *    h = 0/1) sits at bits [16h + 4i, 16h + 4i + 3]. Row stride K/2 bytes.
  *  Scales: FP16, shape [N, K/128], row-major; scale[n, g] covers
  *    k = 128g .. 128g+127 of output row n. Any finite value is allowed
  *    (zero and subnormal included); non-finite scales give unspecified results.
@@ -86,7 +91,8 @@ typedef enum {
 } lowbit_status;
 
 typedef enum { LOWBIT_F16 = 0, LOWBIT_BF16 = 1, LOWBIT_F32 = 2, LOWBIT_NONE = 3 } lowbit_dtype;
-typedef enum { LOWBIT_BINARY_1BIT = 1, LOWBIT_TERNARY_INT2 = 2, LOWBIT_TERNARY_BASE3 = 3 } lowbit_format;
+typedef enum { LOWBIT_BINARY_1BIT = 1, LOWBIT_TERNARY_INT2 = 2, LOWBIT_TERNARY_BASE3 = 3,
+               LOWBIT_INT4_ZP = 4 } lowbit_format;
 typedef enum { LOWBIT_ACT_NONE = 0, LOWBIT_ACT_GELU_ERF = 1 } lowbit_activation;
 
 /* ABI version of the loaded library (LOWBIT_ABI_VERSION). */
@@ -113,8 +119,9 @@ int32_t lowbit_init(void);
 int32_t lowbit_debug_force_variant(const char* name);
 
 /* Bytes of packed codes for an N x K matrix: N*K/4 (ternary), N*K/8 (binary),
- * N*ceil(K/5) (base-3); -1 for a bad format or a K that breaks the packing
- * rule (ternary K % 16, binary K % 32) or N, K < 1 or >= 2^31. */
+ * N*ceil(K/5) (base-3), N*K/2 (4-bit); -1 for a bad format or a K that
+ * breaks the packing rule (ternary K % 16, binary K % 32, 4-bit K % 8) or
+ * N, K < 1 or >= 2^31. */
 int64_t lowbit_packed_bytes(int32_t format, int64_t N, int64_t K);
 
 /* Number of FP16 scales, N * K / group; -1 if group != 128 or K % group != 0. */
@@ -150,7 +157,18 @@ int32_t pack_binary(const int8_t* codes, int64_t N, int64_t K, uint8_t* packed,
 int32_t pack_base3(const int8_t* codes, int64_t N, int64_t K, uint8_t* packed,
                    int32_t* invalid_count, void* stream);
 
-/* Inverse of the packers: packed (format layout above) -> int8 codes[N][K].
+/* Pack 4-bit codes q[N][K] (uint8 values 0..15) into the 4-bit layout above
+ * (the 4-bit group-quantised weights of the pipeline's text encoder, "Como
+ * Bonsai Ternary 4B revoluciona la difusion texto-imagen", section
+ * "Arquitectura de despliegue y eficiencia en tiempo de ejecucion"; the
+ * layout is this library's own). packed: N*K/2 bytes. K % 8 == 0. Values
+ * above 15 are counted in invalid_count and stored as 0. Alignment and
+ * ownership as pack_ternary. */
+int32_t pack_int4(const uint8_t* codes, int64_t N, int64_t K, uint8_t* packed,
+                  int32_t* invalid_count, void* stream);
+
+/* Inverse of the packers: packed (format layout above) -> int8 codes[N][K]
+ * (for LOWBIT_INT4_ZP the codes are the unsigned values 0..15).
  * Ternary code 10 and base-3 bytes 243 .. 255 are invalid: their values
  * decode to 0 and are counted, one per value, in invalid_count (nullable).
  * Binary has no invalid pattern (count set to 0). codes and packed are
@@ -250,6 +268,34 @@ int32_t lowbit_gemm_noalloc(int32_t format,
                             const void* bias, int32_t bias_dtype,
                             void* Y, int32_t y_dtype, int64_t ldy,
                             int32_t activation, void* stream);
+
+/* Workspace bytes lowbit_gemm_int4 needs: the per-group row sums of X,
+ * K/128 x (M rounded up to 128, plus 128) FP32 values; 0 for a bad shape. */
+size_t lowbit_gemm_int4_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* The 4-bit group-quantised linear (any M), with a zero point per group:
+ *
+ *   Y[m, n] = act( sum_k X[m, k] * s[n, k/128] * (q[n, k] - z[n, k/128]) + bias[n] )
+ *
+ * with FP32 accumulation and one RNE cast, for the text encoder's 4-bit
+ * weights ("Como Bonsai Ternary 4B revoluciona la difusion texto-imagen",
+ * section "Arquitectura de despliegue y eficiencia en tiempo de ejecucion").
+ * Arguments as lowbit_gemm, with W_packed in the 4-bit layout ([N][K/2]
+ * bytes), `zeros` FP16 [N][K/128] (2-byte aligned, finite) beside `scales`,
+ * and a workspace of lowbit_gemm_int4_workspace_bytes (256-byte aligned;
+ * its contents need no initialisation and are overwritten; calls that can
+ * run concurrently must not share it). X must span less than 4 GiB.
+ * Accuracy contract per element: |Y - exact| <= 1e-3 * sum_k |x_k w_k| + 1e-5
+ * + 2^-19 * (128 + max|z|) * sum_k |x_k s_k| (plus half an output ulp for
+ * FP16/BF16 outputs): the kernel accumulates sum x (128 + q) and takes
+ * (128 + z) times the group's activation sum off it, so the FP32 roundings
+ * of those two sums add the last term, which matters only when |q - z| is
+ * small against 128. Deterministic. */
+int32_t lowbit_gemm_int4(const void* X, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx,
+                         const uint8_t* W_packed, const void* scales, const void* zeros, int32_t group,
+                         int64_t N, const void* bias, int32_t bias_dtype,
+                         void* Y, int32_t y_dtype, int64_t ldy, int32_t activation,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* Several independent linears of one shape in one launch: problem z computes
  *

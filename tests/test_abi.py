@@ -33,7 +33,8 @@ def test_header_declares_expected_entry_points():
                  "lowbit_gemm", "lowbit_gemm_grouped", "lowbit_gemm_grouped_workspace_bytes",
                  "lowbit_gemm_workspace_bytes", "lowbit_packed_bytes", "lowbit_scale_count",
                  "lowbit_status_string", "lowbit_abi_version", "lowbit_init", "lowbit_gelu",
-                 "lowbit_debug_force_variant"):
+                 "lowbit_debug_force_variant", "lowbit_gemm_noalloc", "pack_int4", "lowbit_gemm_int4",
+                 "lowbit_gemm_int4_workspace_bytes"):
         assert want in names
 
 
@@ -62,6 +63,12 @@ def test_host_only_queries(L):
     assert L.lowbit_packed_bytes(b.BASE3, 5, 7) == 10
     assert L.lowbit_packed_bytes(b.BASE3, 1, 0) == -1
     assert L.lowbit_packed_bytes(b.BASE3, 1, 1 << 31) == -1
+    assert L.lowbit_packed_bytes(b.INT4, 2560, 9728) == 2560 * 4864
+    assert L.lowbit_packed_bytes(b.INT4, 4, 12) == -1          # K % 8
+    # 4-bit row sums: one float per 128-group and padded row
+    assert L.lowbit_gemm_int4_workspace_bytes(512, 2560, 9728) == 76 * (512 + 128) * 4
+    assert L.lowbit_gemm_int4_workspace_bytes(1, 64, 256) == 2 * 256 * 4
+    assert L.lowbit_gemm_int4_workspace_bytes(1, 64, 200) == 0
     assert L.lowbit_scale_count(3072, 9216, 128) == 3072 * 72
     assert L.lowbit_scale_count(3072, 9216, 64) == -1
     for s in range(10):
@@ -176,6 +183,45 @@ def test_argument_errors_before_any_device_work(L):
     assert L.lowbit_gemm_grouped_workspace_bytes(0, b.TERNARY, 16, 64, 256) == 0
     assert L.lowbit_gemm_grouped_workspace_bytes(9, b.TERNARY, 16, 64, 256) == 0
     assert L.lowbit_gelu(P, P, b.NONE, 10, None) == b.ERR_DTYPE
+
+
+def test_int4_argument_errors_before_any_device_work(L):
+    """lowbit_gemm_int4 runs every check of lowbit_gemm, then its own: zero
+    points present and aligned, K/2 bytes a packed row, the row-sum
+    workspace present, large enough, aligned and apart from every operand."""
+    import bit_weight_gemm_int2_amd as b
+    P = 1 << 20
+    PX, PW, PS, PY, PB, PZ, PWS = (k << 36 for k in range(1, 8))
+    need = L.lowbit_gemm_int4_workspace_bytes(16, 64, 256)
+    good = dict(X=PX, xd=b.BF16, M=16, K=256, ldx=256, W=PW, S=PS, Z=PZ, group=128, N=64, bias=None, bd=b.NONE,
+                Y=PY, yd=b.BF16, ldy=64, act=0, ws=PWS, wsb=need)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return L.lowbit_gemm_int4(a["X"], a["xd"], a["M"], a["K"], a["ldx"], a["W"], a["S"], a["Z"], a["group"],
+                                  a["N"], a["bias"], a["bd"], a["Y"], a["yd"], a["ldy"], a["act"], a["ws"],
+                                  a["wsb"], None)
+
+    assert call(Z=None) == b.ERR_NULL
+    assert call(X=None) == b.ERR_NULL
+    assert call(xd=b.F32) == b.ERR_DTYPE
+    assert call(group=64) == b.ERR_GROUP
+    assert call(K=200, ldx=200) == b.ERR_SHAPE
+    assert call(M=0) == b.ERR_SHAPE
+    # packed 4-bit weights spanning 4 GiB: N * K / 2 bytes (2^20 * 2^13 / 2 = 2^32)
+    assert call(N=1 << 20, ldy=1 << 20, K=1 << 13, ldx=1 << 13) == b.ERR_SHAPE
+    assert call(Z=PZ + 1) == b.ERR_ALIGN
+    assert call(ws=None) == b.ERR_WORKSPACE
+    assert call(wsb=need - 4) == b.ERR_WORKSPACE
+    assert call(ws=PWS + 16) == b.ERR_ALIGN
+    assert call(Y=PW + 64 * 100) == b.ERR_OVERLAP                 # into the second half of the K/2-byte rows
+    assert call(Y=PZ) == b.ERR_OVERLAP
+    for where in (PX, PW + 64 * 100, PS, PZ, PY + 64):
+        assert call(ws=(where & ~255) - 256, wsb=max(need, 512)) == b.ERR_OVERLAP, hex(where)
+    assert call(ws=PB, wsb=need, bias=PB + need - 4, bd=b.F32) == b.ERR_OVERLAP
+    assert L.pack_int4(None, 4, 16, P, None, None) == b.ERR_NULL
+    assert L.pack_int4(P, 4, 12, P << 1, None, None) == b.ERR_SHAPE
+    assert L.pack_int4(PX, 4, 16, PX + 16, None, None) == b.ERR_OVERLAP
 
 
 def test_variant_hook_names(L):

@@ -231,3 +231,68 @@ def config5_activations(M: int = 4608, seed: int = 4):
     """One bf16 X per distinct K (3072, 9216, 12288), shared by every linear with that K."""
     g = generator(10_000 + seed)
     return {K: activations(g, M, K, "bf16") for K in (HIDDEN, MLP, HIDDEN + MLP)}
+
+
+# ---------------------------------------------------------------------------
+# 4-bit text-encoder weights
+# ---------------------------------------------------------------------------
+# The pages compress the Qwen3-4B text encoder to 4-bit HQQ ("Cómo Bonsai
+# Ternary 4B revoluciona la difusión texto-imagen", section "Arquitectura de
+# despliegue y eficiencia en tiempo de ejecución"). They give neither its
+# shapes nor the HQQ layout; the shapes below are those of the public
+# Qwen3-4B architecture (hidden 2560, 32 query and 8 key/value heads of 128,
+# MLP 9728), the layout is 4-bit codes with an FP16 scale and zero point per
+# 128 weights along K, and 512 prompt tokens stand in for a prompt.
+TE_HIDDEN, TE_Q, TE_KV, TE_MLP, TE_TOKENS = 2560, 4096, 1024, 9728, 512
+
+
+def int4_codes(g: np.random.Generator, N: int, K: int) -> np.ndarray:
+    """Unsigned 4-bit codes, uniform over 0..15, uint8 [N, K]."""
+    return g.integers(0, 16, size=(N, K), dtype=np.uint8)
+
+
+def int4_zeros(g: np.random.Generator, N: int, K: int, center: float = 7.5, std: float = 0.5) -> np.ndarray:
+    """FP16 zero points [N, K/128]: center + N(0, std), drawn in float32."""
+    assert K % GROUP == 0
+    z = np.float32(center) + g.standard_normal((N, K // GROUP), dtype=np.float32) * np.float32(std)
+    return z.astype(np.float16)
+
+
+@dataclass
+class Int4Linear:
+    """One synthetic 4-bit linear: X[M,K] (16-bit bits), q[N,K] in 0..15,
+    scales and zero points [N,K/128] FP16."""
+    name: str
+    M: int
+    N: int
+    K: int
+    x_dtype: str
+    y_dtype: str
+    x: np.ndarray
+    q: np.ndarray
+    scales: np.ndarray
+    zeros: np.ndarray
+    bias: Optional[np.ndarray] = None
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+
+def make_int4_linear(name, M, N, K, x_dtype="bf16", y_dtype=None, seed=0, with_bias=False, g=None, x=None,
+                     zero_center=7.5, zero_std=0.5, scale_std=0.003) -> Int4Linear:
+    """Draw order: X, codes, scales (|N(0, scale_std)| + 1e-4), zero points, bias."""
+    g = generator(seed) if g is None else g
+    if x is None:
+        x = activations(g, M, K, x_dtype)
+    q = int4_codes(g, N, K)
+    scales = group_scales(g, N, K, offset=1e-4, std=scale_std)
+    zeros = int4_zeros(g, N, K, zero_center, zero_std)
+    b = bias_f16(g, N) if with_bias else None
+    return Int4Linear(name, M, N, K, x_dtype, y_dtype or x_dtype, x, q, scales, zeros, b)
+
+
+def text_encoder_shapes():
+    """(name, N, K) of the seven linears of one text-encoder layer."""
+    return [("q", TE_Q, TE_HIDDEN), ("k", TE_KV, TE_HIDDEN), ("v", TE_KV, TE_HIDDEN), ("o", TE_HIDDEN, TE_Q),
+            ("gate", TE_MLP, TE_HIDDEN), ("up", TE_MLP, TE_HIDDEN), ("down", TE_HIDDEN, TE_MLP)]
