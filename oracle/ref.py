@@ -33,6 +33,13 @@ Readings where the pages are silent (each is listed in the design notes):
   k = 5j .. 5j+4 with ``d[5j]`` least significant, rows of ceil(K/5) bytes; bytes
   243 .. 255 are invalid. The pages print no such layout; see the section
   "Base-3 storage" below.
+* Quantiser (FP16 weights -> t and s): the pages name BinaryConnect and Ternary
+  Weight Networks (page "cuantificación de modelos de difusión para inferencia
+  local en dispositivos edge", section "Fundamentos Teóricos") but do not say
+  how the released weights were quantised. ``quantize`` applies those two rules
+  per 128-group; it is pinned to the rules' own definition (hand-derived groups,
+  exact rationals, round trips), and its agreement with the pages' actual
+  quantiser is parity unpinned.
 * Groups run along K inside one output row; K must be a multiple of 128.
 * The bias, when present, is added once in the output row sum.
 * Output cast: round to nearest, ties to even.
@@ -411,6 +418,62 @@ def magnitude_int4(x_bits: np.ndarray, x_dtype: str, q: np.ndarray, scales: np.n
     if bias is not None:
         Mg = Mg + np.abs(np.asarray(bias, dtype=np.float16).astype(np.float64))[None, :]
     return Mg
+
+
+# ---------------------------------------------------------------------------
+# Quantiser: FP16 weights -> (t, s) per 128-group
+#
+# The pages do not say how t and s are obtained from trained weights. Page
+# "cuantificación de modelos de difusión para inferencia local en dispositivos
+# edge", section "Fundamentos Teóricos", names the two lines of work the
+# variants descend from, BinaryConnect (binary weights, Courbariaux et al.
+# 2015) and Ternary Weight Networks (Li et al. 2016), and says the FP16 group
+# scale restores each group's range. Reading taken here (parity of the method
+# itself against the pages is unpinned; the rule below is pinned to its own
+# definition), applied to each group of 128 weights of a row:
+# * ternary (TWN): a weight is kept when |w| > 0.7 * mean|w| over the group;
+#   t = sign(w) for kept weights and 0 otherwise; s = the mean of |w| over the
+#   kept weights (0 when none is kept);
+# * binary (BinaryConnect's deterministic sign with a group scale): t = +1 when
+#   w >= 0 (so -0.0 gives +1) and -1 otherwise; s = mean|w| over the group
+#   (the scale that minimises sum (w - s t)^2 for those signs);
+# * s is the FP16 value nearest the exact mean (ties to even);
+# * a non-finite weight (NaN or infinity) is counted and acts as +0.0.
+#
+# Exactness: every |w| is an FP16 value, a multiple of 2^-24 below 2^16, so
+# sums of up to 128 of them are multiples of 2^-24 below 2^23 and are exact in
+# float64 (at most 47 significant bits), whatever the order. The threshold test
+# |w| > 0.7 mean|w| is 1280 |w| > 7 sum|w| (both sides exact in float64). The
+# mean of the kept weights is sum/c with c <= 128: float64 division rounds it
+# once, and rounding that to FP16 cannot differ from rounding the exact
+# quotient, because a quotient with odd denominator part <= 127 that is not
+# itself a 12-bit number lies at least 2^-19 (relative) from every FP16
+# rounding midpoint, far beyond the 2^-53 of the float64 rounding.
+# ---------------------------------------------------------------------------
+
+def quantize(w_bits: np.ndarray, fmt: str, group: int = GROUP) -> Tuple[np.ndarray, np.ndarray, int]:
+    """FP16 weights [N, K] (uint16 bit patterns) -> (int8 t [N, K], uint16 FP16
+    scale bits [N, K/group], number of non-finite weights)."""
+    w = decode(np.asarray(w_bits, dtype=np.uint16), "f16")
+    N, K = w.shape
+    if K % group:
+        raise ValueError("K must be a multiple of the group size")
+    bad = ~np.isfinite(w)
+    w = np.where(bad, 0.0, w)
+    a = np.abs(w).reshape(N, K // group, group)
+    total = a.sum(axis=2)                                   # exact (see above)
+    if fmt == "ternary":
+        keep = 1280.0 * a > 7.0 * total[:, :, None]          # |w| > 0.7 * mean|w|
+        count = keep.sum(axis=2)
+        kept = np.where(keep, a, 0.0).sum(axis=2)
+        mean = np.where(count > 0, kept / np.maximum(count, 1), 0.0)
+        t = np.where(keep.reshape(N, K), np.sign(w), 0.0)
+    elif fmt == "binary":
+        mean = total / group
+        t = np.where(w >= 0.0, 1.0, -1.0)
+    else:
+        raise ValueError(fmt)
+    return t.astype(np.int8), encode(mean, "f16"), int(bad.sum())
 
 
 # ---------------------------------------------------------------------------

@@ -518,3 +518,119 @@ def test_int4_linear_against_exact_rationals(K):
             exact = sum(Fraction(float(X[m, kk])) * Fraction(float(s[n, kk // 128])) *
                         (Fraction(int(q[n, kk])) - Fraction(float(z[n, kk // 128]))) for kk in range(K))
             assert abs(Fraction(A[m, n]) - exact) <= abs(exact) * Fraction(2) ** -45 + Fraction(2) ** -60
+
+
+# -------------------------------------------------------------- quantiser ---
+
+def _runs(runs):
+    return [v for n, v in runs for _ in range(n)]
+
+
+def test_quantize_hand_cases(golden_dir):
+    """Hand-derived groups: the threshold (strict, with an exact tie), the kept
+    mean and its rounding (both kinds of midpoint), zero and subnormal means,
+    signed zeros, non-finite weights."""
+    g = _golden(golden_dir, "quantize_groups.json")
+    for case in g["cases"]:
+        w = np.array([[int(h, 16) for h in _runs(case["w"])]], dtype=np.uint16)
+        t, s, bad = oracle.quantize(w, case["fmt"])
+        assert t[0].tolist() == _runs(case["t"]), case["name"]
+        assert int(s[0, 0]) == int(case["s_hex"], 16), case["name"]
+        assert bad == case["nonfinite"], case["name"]
+
+
+def _f16_nearest_exact(q: Fraction) -> int:
+    """FP16 bits of the value nearest the non-negative rational q (ties to an
+    even bit pattern), by bisection over the ordered finite FP16 values."""
+    lo, hi = 0, 0x7BFF
+    val = lambda b: Fraction(float(np.array(b, dtype=np.uint16).view(np.float16)))
+    if q >= val(hi):
+        return hi
+    while hi - lo > 1:                      # val(lo) <= q < val(hi)
+        mid = (lo + hi) // 2
+        if val(mid) <= q:
+            lo = mid
+        else:
+            hi = mid
+    dl, dh = q - val(lo), val(hi) - q
+    if dl != dh:
+        return lo if dl < dh else hi
+    return lo if lo % 2 == 0 else hi
+
+
+@pytest.mark.parametrize("fmt", ["ternary", "binary"])
+def test_quantize_against_exact_rationals(fmt):
+    """Random groups (normal, with outliers, many exact zeros, subnormal) against
+    the rule carried out in exact rational arithmetic with a brute-force FP16
+    rounding."""
+    g = wl.generator(31)
+    rows = [wl.fp16_weights(g, 3, 256), wl.fp16_weights(g, 3, 256, outliers=0.05),
+            wl.fp16_weights(g, 2, 256, std=1e-6)]
+    z = wl.fp16_weights(g, 2, 256)
+    z[:, ::3] = 0
+    rows.append(z)
+    w = np.concatenate(rows)
+    t, s, bad = oracle.quantize(w, fmt)
+    assert bad == 0
+    vals = w.view(np.float16).astype(np.float64)
+    for n in range(w.shape[0]):
+        for gi in range(2):
+            grp = [Fraction(float(v)) for v in vals[n, 128 * gi:128 * gi + 128]]
+            total = sum(abs(v) for v in grp)
+            if fmt == "ternary":
+                keep = [abs(v) > Fraction(7, 10) * total / 128 for v in grp]
+                kept = [abs(v) for v, k in zip(grp, keep) if k]
+                mean = sum(kept) / len(kept) if kept else Fraction(0)
+                expect_t = [(1 if v > 0 else -1) if k else 0 for v, k in zip(grp, keep)]
+            else:
+                mean = total / 128
+                expect_t = [1 if v >= 0 else -1 for v in grp]
+            assert int(s[n, gi]) == _f16_nearest_exact(mean)
+            assert t[n, 128 * gi:128 * gi + 128].tolist() == expect_t
+
+
+@pytest.mark.parametrize("fmt", ["ternary", "binary"])
+def test_quantize_recovers_quantised_weights(fmt):
+    """Weights that already are s * t (FP16 s per group) come back unchanged:
+    ternary keeps exactly the non-zero ones (|w| = s > 0.7 * p s for a non-zero
+    fraction p <= 1), binary's mean|w| is s."""
+    g = wl.generator(32)
+    N, K = 6, 512
+    t0 = wl.ternary_codes(g, N, K, 0.35) if fmt == "ternary" else wl.binary_codes(g, N, K)
+    s0 = wl.group_scales(g, N, K, offset=1e-3)
+    w = (np.repeat(s0.astype(np.float64), 128, axis=1) * t0).astype(np.float16).view(np.uint16)
+    t, s, bad = oracle.quantize(w, fmt)
+    assert bad == 0 and np.array_equal(t, t0) and np.array_equal(s, s0.view(np.uint16))
+
+
+def test_quantize_invariants():
+    """Scaling by a power of two scales s and keeps t; negation flips t and keeps
+    s (ternary; binary away from zero)."""
+    g = wl.generator(33)
+    w = wl.fp16_weights(g, 4, 384, std=0.5)
+    wf = w.view(np.float16)
+    for fmt in ("ternary", "binary"):
+        t, s, _ = oracle.quantize(w, fmt)
+        t2, s2, _ = oracle.quantize((wf * np.float16(4)).view(np.uint16), fmt)
+        assert np.array_equal(t2, t)
+        assert np.array_equal(s2.view(np.float16), s.view(np.float16) * np.float16(4))
+        tn, sn, _ = oracle.quantize((-wf).view(np.uint16), fmt)
+        assert np.array_equal(sn, s)
+        nz = wf != 0
+        assert np.array_equal(tn[nz], -t[nz])
+
+
+def test_quantize_planted_rule_changes_are_caught(golden_dir):
+    """The hand cases fail a threshold taken with >= and a mean over the whole
+    group instead of the kept weights (mistakes planted in a copy of the rule)."""
+    g = _golden(golden_dir, "quantize_groups.json")
+    tie = next(c for c in g["cases"] if c["name"] == "ternary: tie at the threshold")
+    w = np.array([[int(h, 16) for h in _runs(tie["w"])]], dtype=np.float16)
+    a = np.abs(w.view(np.uint16).view(np.float16).astype(np.float64))
+    total = a.sum()
+    keep_ge = 1280.0 * a >= 7.0 * total                      # planted: >= instead of >
+    assert keep_ge.sum() != sum(n for n, v in tie["t"] if v != 0)
+    first = g["cases"][0]
+    w1 = np.array([int(h, 16) for h in _runs(first["w"])], dtype=np.uint16).view(np.float16).astype(np.float64)
+    whole_mean = oracle.encode(np.array([np.abs(w1).mean()]), "f16")[0]   # planted: mean of all
+    assert int(whole_mean) != int(first["s_hex"], 16)

@@ -296,3 +296,15 @@ def text_encoder_shapes():
     """(name, N, K) of the seven linears of one text-encoder layer."""
     return [("q", TE_Q, TE_HIDDEN), ("k", TE_KV, TE_HIDDEN), ("v", TE_KV, TE_HIDDEN), ("o", TE_HIDDEN, TE_Q),
             ("gate", TE_MLP, TE_HIDDEN), ("up", TE_MLP, TE_HIDDEN), ("down", TE_HIDDEN, TE_MLP)]
+
+
+def fp16_weights(g: np.random.Generator, N: int, K: int, std: float = 0.02, outliers: float = 0.0) -> np.ndarray:
+    """Dense FP16 weights [N, K] as uint16 bit patterns, the input of the
+    quantiser: a normal with standard deviation ``std`` drawn in float32 and
+    rounded to FP16 (the spread of a trained transformer's linear weights is of
+    that order), and, when ``outliers`` > 0, that fraction of the weights
+    multiplied by 8 (the few large weights trained layers carry)."""
+    w = g.standard_normal((N, K), dtype=np.float32) * np.float32(std)
+    if outliers:
+        w = np.where(g.random((N, K), dtype=np.float32) < np.float32(outliers), w * np.float32(8.0), w)
+    return np.ascontiguousarray(w.astype(np.float16)).view(np.uint16)
