@@ -475,6 +475,73 @@ def bench_base3_transcode(torch, lb, reps=10):
                            frac_hbm_peak=round(gbs3 / PEAK_HBM_GBS, 4)))
 
 
+def bench_quantize(torch, lb, reps=10):
+    """Load-time quantisation of the 100-linear sweep's dense FP16 weights into
+    ternary codes and group scales (lowbit_quantize): 5.66 GB of FP16 read,
+    0.75 GB of codes and scales written per pass. Per linear (100 launches,
+    each on its own buffers, replayed from a HIP graph) and per distinct K over
+    the rows of every linear with that K stored back to back (3 launches; the
+    rule is row-local, so that is the same quantisation). Weights: normal with
+    standard deviation 0.02, drawn on the device (torch, seed 15)."""
+    import workloads as wl
+    shapes = wl.mmdit_linear_shapes()
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(15)
+    ins = []
+    for _, N, K in shapes:
+        w = torch.randn((N, K), generator=gen, device="cuda", dtype=torch.float32).mul_(0.02).half()
+        ins.append((w, N, K))
+    outs = [(torch.empty((N, K // 4), dtype=torch.uint8, device="cuda"),
+             torch.empty((N, K // 128), dtype=torch.float16, device="cuda")) for _, N, K in ins]
+    rd = sum(2 * N * K for _, N, K in ins)
+    wr = sum(N * K // 4 + 2 * N * K // 128 for _, N, K in ins)
+
+    def timed(one_pass):
+        one_pass()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            one_pass()
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            graph.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / reps
+        del graph
+        return ms, (rd + wr) / (ms * 1e-3) / 1e9
+
+    def per_linear():
+        for (w, N, K), o in zip(ins, outs):
+            lb.quantize(w, "ternary", check=False, out=o)
+    ms1, gbs1 = timed(per_linear)
+    del outs
+    stacked = {}
+    for K in sorted({K for _, _, K in ins}):
+        stacked[K] = torch.cat([w for w, _, k in ins if k == K], 0)
+    del ins
+    souts = {K: (torch.empty((w.shape[0], K // 4), dtype=torch.uint8, device="cuda"),
+                 torch.empty((w.shape[0], K // 128), dtype=torch.float16, device="cuda"))
+             for K, w in stacked.items()}
+
+    def per_k():
+        for K, w in stacked.items():
+            lb.quantize(w, "ternary", check=False, out=souts[K])
+    ms3, gbs3 = timed(per_k)
+    del stacked, souts
+    torch.cuda.empty_cache()
+    return dict(bytes_read=rd, bytes_written=wr,
+                per_linear=dict(launches=len(shapes), ms_per_pass=round(ms1, 4), GBps=round(gbs1, 1),
+                                frac_hbm_peak=round(gbs1 / PEAK_HBM_GBS, 4)),
+                per_k=dict(launches=3, ms_per_pass=round(ms3, 4), GBps=round(gbs3, 1),
+                           frac_hbm_peak=round(gbs3 / PEAK_HBM_GBS, 4)))
+
+
 def traffic_probe(torch, lb):
     """Workload for the rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE passes: first a
     plain 256 MiB device copy (calibration: its byte counts are known), then two
@@ -806,6 +873,7 @@ def main():
     small_grouped = None if args.no_small else bench_small(torch, lb, fuse_qkv=True, grouped=True)
     small_single = None if (args.no_small or args.no_context) else bench_small_single(torch, lb)
     base3 = None if args.no_small else bench_base3_transcode(torch, lb)
+    quant = None if args.no_small else bench_quantize(torch, lb)
     cpu = None if args.no_cpu else cpu_baseline()
     out = {
         "metric": METRIC,
@@ -851,6 +919,7 @@ def main():
         "small_m_grouped": small_grouped,
         "small_m_binary_single": small_single,
         "base3_to_int2_sweep": base3,
+        "quantize_sweep": quant,
     }
     print(json.dumps(out), flush=True)
 

@@ -59,6 +59,7 @@ SIGNATURES = [
     ("lowbit_gemm_int4_workspace_bytes", _SZ, [_I64, _I64, _I64]),
     ("lowbit_gemm_int4", _I32, [_P, _I32, _I64, _I64, _I64, _P, _P, _P, _I32, _I64,
                                 _P, _I32, _P, _I32, _I64, _I32, _P, _SZ, _P]),
+    ("lowbit_quantize", _I32, [_I32, _P, _I64, _I64, _I64, _P, _P, _P, _P]),
 ]
 MAX_GROUP = 8
 
@@ -240,6 +241,37 @@ def gemm_int4(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, zeros
         out.stride(0), _ACT[activation], workspace.data_ptr(), workspace.numel() * workspace.element_size(),
         _stream(stream)), "lowbit_gemm_int4")
     return out
+
+
+def quantize(w: torch.Tensor, fmt, check: bool = True, out=None, stream=None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Dense FP16 weights [N, K] (row stride may exceed K) -> (packed uint8
+    [N, K/4] or [N, K/8], fp16 scales [N, K/128]) by lowbit_quantize, into
+    `out` = (packed, scales) when given. With check, waits for the device and
+    raises on NaN or infinite weights."""
+    _cuda(w, "w")
+    if w.dtype != torch.float16 or w.dim() != 2 or w.stride(1) != 1:
+        raise ValueError("w must be a 2-D float16 tensor with unit stride along K")
+    fmt = _FMT[fmt]
+    N, K = w.shape
+    if fmt not in (TERNARY, BINARY) or K % GROUP:
+        raise ValueError("quantize makes ternary or binary codes; K must be a multiple of 128")
+    if out is None:
+        packed = torch.empty((N, _row_bytes(fmt, K)), dtype=torch.uint8, device=w.device)
+        scales = torch.empty((N, K // GROUP), dtype=torch.float16, device=w.device)
+    else:
+        packed, scales = out
+        if (packed.dtype != torch.uint8 or tuple(packed.shape) != (N, _row_bytes(fmt, K))
+                or not packed.is_contiguous() or scales.dtype != torch.float16
+                or tuple(scales.shape) != (N, K // GROUP) or not scales.is_contiguous()):
+            raise ValueError("out must be contiguous (uint8 packed [N, row bytes], float16 scales [N, K/128])")
+    cnt = torch.empty(1, dtype=torch.int32, device=w.device) if check else None
+    _check(lib().lowbit_quantize(fmt, w.data_ptr(), N, K, w.stride(0), packed.data_ptr(), scales.data_ptr(),
+                                 _ptr(cnt), _stream(stream)), "lowbit_quantize")
+    if check:
+        bad = int(cnt.item())
+        if bad:
+            raise ValueError(f"{bad} non-finite weight(s)")
+    return packed, scales
 
 
 def pack_base3(codes: torch.Tensor, check: bool = True, stream=None) -> torch.Tensor:

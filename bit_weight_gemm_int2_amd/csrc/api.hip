@@ -23,6 +23,8 @@ hipError_t launch_gemm(int fmt, bool x_bf16, GemmArgs a, int num_cu, int variant
                        const GemmGroup* group = nullptr, int count = 1);
 hipError_t launch_gelu(const void* in, void* out, int dtype, int64_t count, hipStream_t st);
 hipError_t launch_gemm_int4(bool x_bf16, GemmArgs a, int num_cu, hipStream_t st);
+hipError_t launch_quantize(int fmt, const uint16_t* W, int64_t ldw, int64_t N, int64_t K, uint8_t* packed,
+                           uint16_t* scales, int32_t* counter, hipStream_t st);
 int64_t int4_rows(int64_t M);
 size_t small_workspace_bytes(int M, int N, int K, int num_cu, int variant, int count = 1);
 bool small_path(int M, int N, int K, int variant, int count = 1);
@@ -241,6 +243,28 @@ int32_t unpack_lowbit(int32_t format, const uint8_t* packed, int64_t N, int64_t 
   if (st) return st;
   hipError_t e = lowbit::launch_unpack(kernel_format(format), packed, N, K, codes, invalid_count,
                                        (hipStream_t)stream);
+  return e == hipSuccess ? LOWBIT_OK : LOWBIT_ERR_HIP;
+}
+
+int32_t lowbit_quantize(int32_t format, const void* W, int64_t N, int64_t K, int64_t ldw, uint8_t* packed,
+                        void* scales, int32_t* nonfinite_count, void* stream) {
+  if (format != LOWBIT_TERNARY_INT2 && format != LOWBIT_BINARY_1BIT) return LOWBIT_ERR_DTYPE;
+  if (!W || !packed || !scales) return LOWBIT_ERR_NULL;
+  if (N < 1 || K < LOWBIT_GROUP || N >= kMaxDim || K >= kMaxDim || K % LOWBIT_GROUP || ldw < K || ldw >= kMaxDim)
+    return LOWBIT_ERR_SHAPE;
+  if (!aligned(W, 16) || ldw % 8 || !aligned(packed, 16) || !aligned(scales, 2) ||
+      (nonfinite_count && !aligned(nonfinite_count, 4)))
+    return LOWBIT_ERR_ALIGN;
+  const int64_t wbytes = ((N - 1) * ldw + K) * 2, pbytes = lowbit_packed_bytes(format, N, K),
+                sbytes = N * (K / LOWBIT_GROUP) * 2;
+  if (overlaps(packed, pbytes, W, wbytes) || overlaps(scales, sbytes, W, wbytes) ||
+      overlaps(scales, sbytes, packed, pbytes) || overlaps(nonfinite_count, 4, W, wbytes) ||
+      overlaps(nonfinite_count, 4, packed, pbytes) || overlaps(nonfinite_count, 4, scales, sbytes))
+    return LOWBIT_ERR_OVERLAP;
+  int32_t st = current_device(nullptr);
+  if (st) return st;
+  hipError_t e = lowbit::launch_quantize(kernel_format(format), (const uint16_t*)W, ldw, N, K, packed,
+                                         (uint16_t*)scales, nonfinite_count, (hipStream_t)stream);
   return e == hipSuccess ? LOWBIT_OK : LOWBIT_ERR_HIP;
 }
 

@@ -167,6 +167,35 @@ int32_t pack_base3(const int8_t* codes, int64_t N, int64_t K, uint8_t* packed,
 int32_t pack_int4(const uint8_t* codes, int64_t N, int64_t K, uint8_t* packed,
                   int32_t* invalid_count, void* stream);
 
+/* Quantise dense FP16 weights into packed codes and FP16 group scales, the
+ * load-time step that makes (t, s) from trained weights. The pages name the
+ * two lines of work the variants come from, BinaryConnect and Ternary Weight
+ * Networks ("cuantificacion de modelos de difusion para inferencia local en
+ * dispositivos edge", section "Fundamentos Teoricos"), with one FP16 scale per
+ * group of 128 ("Representacion y almacenamiento de los pesos ternarios"), but
+ * not the procedure; this library applies those two rules to each group of
+ * 128 weights along K of each row:
+ *   LOWBIT_TERNARY_INT2: a weight is kept when |w| > 0.7 * mean|w| of its
+ *     group; t = sign(w) when kept, else 0; s = mean of the kept |w| (0 when
+ *     none is kept);
+ *   LOWBIT_BINARY_1BIT: t = +1 when w >= 0 (-0.0 included), else -1;
+ *     s = mean|w| of the group;
+ * with s the FP16 value nearest the exact mean (ties to even). Every decision
+ * is exact, so the output is a pure function of the input: bit-identical on
+ * every run and device.
+ *   W        FP16 [N][ldw], the first K columns of each row are the weights;
+ *            16-byte aligned, K <= ldw < 2^31, ldw % 8 == 0
+ *   packed   [N][K/4] (ternary) or [N][K/8] (binary) bytes in the packed
+ *            layout above, 16-byte aligned
+ *   scales   FP16 [N][K/128], 2-byte aligned
+ *   nonfinite_count  nullable device int32 (4-byte aligned): set to the
+ *            number of NaN or infinite weights, which act as +0.0
+ *   N, K     N >= 1; K >= 128, K % 128 == 0; both < 2^31
+ * No output may overlap W or another output (LOWBIT_ERR_OVERLAP); other
+ * formats give LOWBIT_ERR_DTYPE. */
+int32_t lowbit_quantize(int32_t format, const void* W, int64_t N, int64_t K, int64_t ldw,
+                        uint8_t* packed, void* scales, int32_t* nonfinite_count, void* stream);
+
 /* Inverse of the packers: packed (format layout above) -> int8 codes[N][K]
  * (for LOWBIT_INT4_ZP the codes are the unsigned values 0..15).
  * Ternary code 10 and base-3 bytes 243 .. 255 are invalid: their values

@@ -18,6 +18,13 @@ def _declared():
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s+(\w+)\s*\(", text, flags=re.M)))
 
 
+# Tests that pass made-up device addresses: every call in them must fail a
+# host-side check, so on a machine with a GPU (where a call that passed every
+# check would launch a kernel on those addresses) they are skipped.
+made_up_addresses = pytest.mark.skipif(__import__("torch").cuda.device_count() > 0,
+                                       reason="made-up device addresses; CPU-only checks")
+
+
 @pytest.fixture(scope="module")
 def L():
     import bit_weight_gemm_int2_amd as b
@@ -34,7 +41,7 @@ def test_header_declares_expected_entry_points():
                  "lowbit_gemm_workspace_bytes", "lowbit_packed_bytes", "lowbit_scale_count",
                  "lowbit_status_string", "lowbit_abi_version", "lowbit_init", "lowbit_gelu",
                  "lowbit_debug_force_variant", "lowbit_gemm_noalloc", "pack_int4", "lowbit_gemm_int4",
-                 "lowbit_gemm_int4_workspace_bytes"):
+                 "lowbit_gemm_int4_workspace_bytes", "lowbit_quantize"):
         assert want in names
 
 
@@ -76,6 +83,7 @@ def test_host_only_queries(L):
     assert L.lowbit_status_string(99) == b"unknown status"
 
 
+@made_up_addresses
 def test_argument_errors_before_any_device_work(L):
     """Every status that the host check returns before touching the device."""
     import bit_weight_gemm_int2_amd as b
@@ -185,6 +193,7 @@ def test_argument_errors_before_any_device_work(L):
     assert L.lowbit_gelu(P, P, b.NONE, 10, None) == b.ERR_DTYPE
 
 
+@made_up_addresses
 def test_int4_argument_errors_before_any_device_work(L):
     """lowbit_gemm_int4 runs every check of lowbit_gemm, then its own: zero
     points present and aligned, K/2 bytes a packed row, the row-sum
@@ -224,6 +233,44 @@ def test_int4_argument_errors_before_any_device_work(L):
     assert L.pack_int4(PX, 4, 16, PX + 16, None, None) == b.ERR_OVERLAP
 
 
+@made_up_addresses
+def test_quantize_argument_errors_before_any_device_work(L):
+    """lowbit_quantize: format, NULLs, the K and ldw rules, alignment of each
+    pointer and of the row stride, and overlaps between W and each output."""
+    import bit_weight_gemm_int2_amd as b
+    PW, PP, PS, PC = (k << 36 for k in range(1, 5))
+    good = dict(f=b.TERNARY, W=PW, N=64, K=256, ldw=256, P=PP, S=PS, C=PC)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return L.lowbit_quantize(a["f"], a["W"], a["N"], a["K"], a["ldw"], a["P"], a["S"], a["C"], None)
+
+    assert call(f=b.BASE3) == b.ERR_DTYPE
+    assert call(f=b.INT4) == b.ERR_DTYPE
+    assert call(W=None) == b.ERR_NULL
+    assert call(P=None) == b.ERR_NULL
+    assert call(S=None) == b.ERR_NULL
+    assert call(K=192, ldw=192) == b.ERR_SHAPE                   # K % 128
+    assert call(K=0, ldw=8) == b.ERR_SHAPE
+    assert call(N=0) == b.ERR_SHAPE
+    assert call(ldw=128) == b.ERR_SHAPE                          # ldw < K
+    assert call(ldw=260) == b.ERR_ALIGN                          # ldw % 8
+    assert call(W=PW + 8) == b.ERR_ALIGN
+    assert call(P=PP + 4) == b.ERR_ALIGN
+    assert call(S=PS + 1) == b.ERR_ALIGN
+    assert call(C=PC + 2) == b.ERR_ALIGN
+    # W spans (63 * 256 + 256) * 2 = 32 KiB: outputs inside it are refused
+    assert call(P=PW + 32768 - 16) == b.ERR_OVERLAP
+    assert call(S=PW + 100) == b.ERR_OVERLAP
+    assert call(S=PP + 64 * 64 - 2) == b.ERR_OVERLAP             # scales into the packed bytes
+    assert call(C=PS + 4) == b.ERR_OVERLAP
+    # a wider row stride widens the span W covers
+    assert call(ldw=512, P=PW + 40000) == b.ERR_OVERLAP
+    # (that an output just past W is accepted is checked only without a GPU,
+    # in test_valid_call_without_a_gpu_reports_no_device: with a GPU such a
+    # call would launch on these made-up addresses)
+
+
 def test_variant_hook_names(L):
     """The test hook takes exactly the documented names; an unknown one is
     refused and leaves the setting alone."""
@@ -243,6 +290,10 @@ def test_valid_call_without_a_gpu_reports_no_device(L):
     assert L.lowbit_gemm(b.TERNARY, PX, b.BF16, 16, 256, 256, PW, PS, 128, 64, None, b.NONE,
                          PY, b.BF16, 64, 0, None, 0, None) == b.ERR_DEVICE
     assert L.pack_ternary(PX, 4, 16, PW, None, None) == b.ERR_DEVICE
+    assert L.lowbit_quantize(b.TERNARY, PX, 4, 128, 128, PW, PS, None, None) == b.ERR_DEVICE
+    # outputs that start just past W's span (4 rows of 256: 2 KiB) pass the overlap check
+    assert L.lowbit_quantize(b.TERNARY, PX, 4, 256, 256, PX + 2048, PX + 2048 + 256, None, None) == b.ERR_DEVICE
+    assert L.lowbit_quantize(b.BINARY, PX, 4, 256, 256, PX + 2048, PX + 2048 + 128, None, None) == b.ERR_DEVICE
     assert L.lowbit_gelu(PX, PX, b.BF16, 100, None) == b.ERR_DEVICE     # in place is allowed
     assert L.lowbit_gemm_workspace_bytes(b.TERNARY, 16, 3072, 9216) == 0
 
