@@ -325,6 +325,21 @@ def linear(x_bits: np.ndarray, x_dtype: str, t: np.ndarray, scales: np.ndarray,
     return A
 
 
+def linear_f32(x_bits: np.ndarray, x_dtype: str, t: np.ndarray, scales: np.ndarray,
+               bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """The same layer in FP32 arithmetic: exact FP32 dequantisation (s * t),
+    one FP32 BLAS matrix product (sgemm), the bias added in FP32. The CPU
+    baseline's second form; parity uses the float64 ``linear``. Returns
+    float32 values."""
+    X = decode(x_bits, x_dtype).astype(np.float32)           # exact: 16-bit inputs
+    s = np.asarray(scales, dtype=np.float16).astype(np.float32)
+    W = np.repeat(s, GROUP, axis=1) * np.asarray(t).astype(np.float32)   # exact
+    A = X @ W.T
+    if bias is not None:
+        A = A + np.asarray(bias, dtype=np.float16).astype(np.float32)[None, :]
+    return A
+
+
 def magnitude(x_bits: np.ndarray, x_dtype: str, t: np.ndarray, scales: np.ndarray,
               bias: Optional[np.ndarray] = None) -> np.ndarray:
     """sum_k |x[m, k] * w[n, k]| (+ |bias[n]|): the scale of the tolerance."""

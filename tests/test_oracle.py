@@ -634,3 +634,23 @@ def test_quantize_planted_rule_changes_are_caught(golden_dir):
     w1 = np.array([int(h, 16) for h in _runs(first["w"])], dtype=np.uint16).view(np.float16).astype(np.float64)
     whole_mean = oracle.encode(np.array([np.abs(w1).mean()]), "f16")[0]   # planted: mean of all
     assert int(whole_mean) != int(first["s_hex"], 16)
+
+
+def test_linear_f32_form():
+    """The FP32-BLAS form of the layer: bit-equal to the float64 one where every
+    partial sum is exact in FP32 (small integers, power-of-two scales), and
+    inside the tolerance elsewhere."""
+    g = wl.generator(34)
+    M, N, K = 6, 10, 256
+    xi = g.integers(-8, 9, size=(M, K)).astype(np.float32)
+    xb = wl.to_bits(xi, "bf16")
+    t = wl.ternary_codes(g, N, K, 0.35)
+    s = np.ldexp(1.0, g.integers(-3, 3, size=(N, K // 128))).astype(np.float16)
+    b = np.ldexp(1.0, g.integers(-2, 2, size=N)).astype(np.float16)
+    assert np.array_equal(oracle.linear_f32(xb, "bf16", t, s, b).astype(np.float64),
+                          oracle.linear(xb, "bf16", t, s, b))
+    lin = wl.make_linear("f32form", "ternary", 32, 64, 1024, seed=35)
+    A = oracle.linear(lin.x, lin.x_dtype, lin.codes, lin.scales)
+    Mg = oracle.magnitude(lin.x, lin.x_dtype, lin.codes, lin.scales)
+    A32 = oracle.linear_f32(lin.x, lin.x_dtype, lin.codes, lin.scales).astype(np.float64)
+    assert oracle.check(A32, A, Mg, "f32")[0]
