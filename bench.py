@@ -542,6 +542,61 @@ def bench_quantize(torch, lb, reps=10):
                            frac_hbm_peak=round(gbs3 / PEAK_HBM_GBS, 4)))
 
 
+def bench_int4(torch, lb, reps=50):
+    """The text encoder's 4-bit linears (lowbit_gemm_int4): the seven linears
+    of one Qwen3-4B-shaped layer (q, k, v, o, gate, up, down) at 512 prompt
+    tokens, bf16 activations, uniform 4-bit codes, FP16 scales and zero points
+    per 128 (device draws, seed 16), each call with its row-sum pre-pass,
+    back to back on one stream; beside torch.matmul (hipBLASLt) on dense bf16
+    weights of the same shapes."""
+    import workloads as wl
+    M = wl.TE_TOKENS
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(16)
+    layer = []
+    for name, N, K in wl.text_encoder_shapes():
+        q = torch.randint(0, 16, (N, K), generator=gen, device="cuda", dtype=torch.uint8)
+        packed = lb.pack_int4(q)
+        s = (torch.rand((N, K // 128), generator=gen, device="cuda") * 0.003 + 1e-4).half()
+        z = (torch.randn((N, K // 128), generator=gen, device="cuda") * 0.5 + 7.5).half()
+        x = torch.randn((M, K), generator=gen, device="cuda", dtype=torch.float32).bfloat16()
+        y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(max(int(lb.lib().lowbit_gemm_int4_workspace_bytes(M, N, K)), 256), dtype=torch.uint8,
+                         device="cuda")
+        wd = torch.randn((K, N), generator=gen, device="cuda", dtype=torch.float32).bfloat16()
+        layer.append((name, N, K, x, packed, s, z, y, ws, wd))
+        del q
+    flop = sum(2 * M * N * K for _, N, K, *_ in layer)
+
+    def lowbit():
+        for _, N, K, x, packed, s, z, y, ws, _ in layer:
+            lb.gemm_int4(x, packed, s, z, out=y, workspace=ws)
+
+    def dense():
+        for *_, x, _p, _s, _z, _y, _w, wd in layer:
+            torch.matmul(x, wd)
+
+    def timed(fn):
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / reps
+
+    ms, dms = timed(lowbit), timed(dense)
+    del layer
+    torch.cuda.empty_cache()
+    return dict(M=M, linears=7, flop_per_layer=flop, ms_per_layer=round(ms, 4),
+                tflops=round(flop / (ms * 1e-3) / 1e12, 1), dense_bf16_ms=round(dms, 4),
+                dense_bf16_tflops=round(flop / (dms * 1e-3) / 1e12, 1))
+
+
 def traffic_probe(torch, lb):
     """Workload for the rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE passes: first a
     plain 256 MiB device copy (calibration: its byte counts are known), then two
@@ -766,6 +821,17 @@ def dispatch_table(trace_csv: str, kernel: str) -> str:
     return "\n".join(out)
 
 
+def _blas_name() -> str:
+    """The BLAS library numpy uses (for the report)."""
+    try:
+        import numpy as np
+        cfg = np.show_config(mode="dicts")
+        b = cfg.get("Build Dependencies", {}).get("blas", {})
+        return f"{b.get('name', '?')} {b.get('version', '')}".strip()
+    except Exception:
+        return "unknown"
+
+
 def cpu_baseline(seconds_target=10.0):
     """The oracle as it stands (float64 dequantise + BLAS matmul) on a bounded
     sample of the step: the first R rows of the MLP pair (R grown up to all 4608),
@@ -795,9 +861,28 @@ def cpu_baseline(seconds_target=10.0):
         total += time.perf_counter() - t0
         reps += 1
     flop = reps * (2.0 * rows * up.N * up.K + 2.0 * rows * down.N * down.K)
+
+    # the FP32-BLAS form of the same layer (exact FP32 dequantisation, sgemm),
+    # on the same sample, timed for about a third of the time
+    def one32(r):
+        A = oracle.linear_f32(up.x[:r], "bf16", up.codes, up.scales)
+        H = oracle.encode(oracle.gelu(A), "bf16")
+        oracle.linear_f32(H, "bf16", down.codes, down.scales)
+    reps32, total32 = 0, 0.0
+    while total32 < seconds_target / 3 or reps32 == 0:
+        t0 = time.perf_counter()
+        one32(rows)
+        total32 += time.perf_counter() - t0
+        reps32 += 1
+    flop32 = reps32 * (2.0 * rows * up.N * up.K + 2.0 * rows * down.N * down.K)
     return dict(value=round(flop / total / 1e12, 6), unit="TFLOP/s", cores=cores, kind="oracle",
                 sample=f"{reps} pass(es) of the first {rows} of 4608 rows through up-proj, GELU and "
-                       f"down-proj (float64 oracle, {total:.1f} s)")
+                       f"down-proj (float64 oracle, {total:.1f} s)",
+                fp32_blas=dict(value=round(flop32 / total32 / 1e12, 6), unit="TFLOP/s",
+                               sample=f"{reps32} pass(es) of the same rows with the layer in FP32 "
+                                      f"(oracle.linear_f32: exact FP32 dequantisation and sgemm), "
+                                      f"{total32:.1f} s"),
+                blas=_blas_name())
 
 
 def main():
@@ -874,6 +959,7 @@ def main():
     small_single = None if (args.no_small or args.no_context) else bench_small_single(torch, lb)
     base3 = None if args.no_small else bench_base3_transcode(torch, lb)
     quant = None if args.no_small else bench_quantize(torch, lb)
+    int4 = None if args.no_context else bench_int4(torch, lb)
     cpu = None if args.no_cpu else cpu_baseline()
     out = {
         "metric": METRIC,
@@ -920,6 +1006,7 @@ def main():
         "small_m_binary_single": small_single,
         "base3_to_int2_sweep": base3,
         "quantize_sweep": quant,
+        "int4_text_encoder_layer": int4,
     }
     print(json.dumps(out), flush=True)
 
