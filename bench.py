@@ -911,6 +911,8 @@ def main():
                     help="print one kernel's dispatches from a rocprofv3 kernel_trace.csv by grid size")
     ap.add_argument("--stats-table", metavar="STATS_CSV",
                     help="print a rocprofv3 kernel_stats.csv as a markdown table and exit")
+    ap.add_argument("--only", choices=["int4", "quantize", "base3", "small", "small_grouped"],
+                    help="run one of the context legs alone and print its JSON (for kernel traces of it)")
     ap.add_argument("--counter-table", nargs="+", metavar="COUNTER_CSV",
                     help="print per-kernel means of rocprofv3 --pmc counter files and exit")
     args = ap.parse_args()
@@ -942,6 +944,12 @@ def main():
         return
     if args.cpu_configs:
         print(json.dumps(cpu_configs(torch, lb)), flush=True)
+        return
+    if args.only:
+        leg = {"int4": lambda: bench_int4(torch, lb), "quantize": lambda: bench_quantize(torch, lb),
+               "base3": lambda: bench_base3_transcode(torch, lb), "small": lambda: bench_small(torch, lb),
+               "small_grouped": lambda: bench_small(torch, lb, fuse_qkv=True, grouped=True)}[args.only]
+        print(json.dumps({args.only: leg()}), flush=True)
         return
 
     r = bench_large(torch, lb, args.steps, args.warmup, args.settle_s)

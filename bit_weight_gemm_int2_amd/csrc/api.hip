@@ -22,7 +22,7 @@ hipError_t launch_base3_to_int2(const uint8_t* base3, int64_t N, int64_t K, uint
 hipError_t launch_gemm(int fmt, bool x_bf16, GemmArgs a, int num_cu, int variant, hipStream_t st,
                        const GemmGroup* group = nullptr, int count = 1);
 hipError_t launch_gelu(const void* in, void* out, int dtype, int64_t count, hipStream_t st);
-hipError_t launch_gemm_int4(bool x_bf16, GemmArgs a, int num_cu, hipStream_t st);
+hipError_t launch_gemm_int4(bool x_bf16, GemmArgs a, int num_cu, int variant, hipStream_t st);
 hipError_t launch_quantize(int fmt, const uint16_t* W, int64_t ldw, int64_t N, int64_t K, uint8_t* packed,
                            uint16_t* scales, int32_t* counter, hipStream_t st);
 int64_t int4_rows(int64_t M);
@@ -563,7 +563,7 @@ int32_t lowbit_gemm_int4(const void* X, int32_t x_dtype, int64_t M, int64_t K, i
   a.M = (int)M;
   a.Z = (const uint16_t*)zeros;
   a.ldr = lowbit::int4_rows(M);
-  hipError_t e = lowbit::launch_gemm_int4(x_dtype == LOWBIT_BF16, a, num_cu, (hipStream_t)stream);
+  hipError_t e = lowbit::launch_gemm_int4(x_dtype == LOWBIT_BF16, a, num_cu, force_variant(), (hipStream_t)stream);
   return e == hipSuccess ? LOWBIT_OK : LOWBIT_ERR_HIP;
 }
 

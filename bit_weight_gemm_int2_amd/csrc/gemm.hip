@@ -1239,8 +1239,12 @@ hipError_t launch_gemm(int fmt, bool x_bf16, GemmArgs a, int num_cu, int variant
 int64_t int4_rows(int64_t M) { return (M + 127) / 128 * 128 + 128; }
 
 // 4-bit GEMM (any M): the row sums, then the large-M kernel with two stages
-// (a.ws: the row sums, a.ldr: int4_rows(M)).
-hipError_t launch_gemm_int4(bool x_bf16, GemmArgs a, int num_cu, hipStream_t st) {
+// (a.ws: the row sums, a.ldr: int4_rows(M)). Tiles: 128 x 512 (eight waves,
+// one workgroup per CU) or 128 x 256 for narrow N; when those would leave
+// CUs idle (the prompt-sized M of a text encoder: 512 rows make 4 tile
+// rows), 64 x 256 tiles of four waves, 68.5 KiB of LDS, two workgroups per
+// CU. variant: 5 forces the 128-row tiles, 6 the 64-row tiles.
+hipError_t launch_gemm_int4(bool x_bf16, GemmArgs a, int num_cu, int variant, hipStream_t st) {
   const int G = a.K >> 7;
   const int64_t work = (int64_t)G * a.ldr;
   const int64_t blocks = std::min<int64_t>((work + 255) / 256, 65535);
@@ -1248,7 +1252,14 @@ hipError_t launch_gemm_int4(bool x_bf16, GemmArgs a, int num_cu, hipStream_t st)
                      x_bf16 ? 1 : 0);
   const int tm = (a.M + large::BM - 1) / large::BM;
   const int xcd_cu = std::max(1, num_cu / 8);
-  if (a.N >= 2048) {
+  const int64_t wide_tiles = (int64_t)tm * ((a.N + (a.N >= 2048 ? 511 : 255)) / (a.N >= 2048 ? 512 : 256));
+  const bool small = variant == 6 || (variant != 5 && wide_tiles < num_cu);
+  if (small) {
+    const int tm4 = (a.M + 63) / 64, tn = (a.N + 255) / 256;
+    const int xr = xcd_order(a.M, a.N, a.K, FMT_INT4, tm4, tn, 64, 256, 2 * xcd_cu);
+    if (x_bf16) hipLaunchKernelGGL((gemm_large_kernel<true, FMT_INT4, 4, 64, 2>), dim3(tm4 * tn), dim3(256), 0, st, a, tm4, tn, xr);
+    else hipLaunchKernelGGL((gemm_large_kernel<false, FMT_INT4, 4, 64, 2>), dim3(tm4 * tn), dim3(256), 0, st, a, tm4, tn, xr);
+  } else if (a.N >= 2048) {
     const int tn = (a.N + large::bn<8>() - 1) / large::bn<8>();
     const int xr = xcd_order(a.M, a.N, a.K, FMT_INT4, tm, tn, 128, 512, xcd_cu);
     if (x_bf16) hipLaunchKernelGGL((gemm_large_kernel<true, FMT_INT4, 8, 128, 2>), dim3(tm * tn), dim3(512), 0, st, a, tm, tn, xr);

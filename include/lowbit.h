@@ -109,7 +109,8 @@ int32_t lowbit_init(void);
  * the process (all threads), so that tests reach every launch path on the
  * same shapes. name: "auto" or NULL (the automatic choice), "large" (the
  * large-M kernel at any M), "small" (the small-M kernels only), "large-wide"
- * / "large-pair" (one large-M tile configuration), "small-split" (the
+ * / "large-pair" (one large-M tile configuration; for lowbit_gemm_int4 its
+ * 128-row or its 64-row tiles), "small-split" (the
  * small-M column-tile kernel with its K split across workgroups). Results
  * keep the same accuracy contract under every variant, and the workspace
  * queries follow it. The initial value comes from the environment variable

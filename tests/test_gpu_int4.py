@@ -111,6 +111,23 @@ def test_int4_shapes_bf16(lb, M, N, K):
     _assert_parity(_run(lb, lin), lin, lin.name)
 
 
+@pytest.mark.parametrize("variant", ["large-wide", "large-pair"])
+@pytest.mark.parametrize("M,N,K", [(1, 64, 256), (17, 130, 640), (127, 300, 512), (129, 520, 256),
+                                   (300, 2600, 768), (600, 1000, 384)])
+def test_int4_each_tile_configuration(lb, variant, M, N, K):
+    """Both tile configurations of the 4-bit kernel on every shape (forced):
+    128-row tiles ("large-wide") and 64-row tiles, two workgroups per CU
+    ("large-pair"); ragged rows and columns on both."""
+    banner(f"int4 gemm {variant} {M}x{N}x{K}")
+    lin = wl.make_int4_linear(f"i4v_{M}x{N}x{K}", M, N, K, "bf16", seed=M + 3 * N + K, with_bias=True)
+    lb.force_variant(variant)
+    try:
+        Y = _run(lb, lin, act="gelu" if M % 2 else None)
+    finally:
+        lb.force_variant(None)
+    _assert_parity(Y, lin, f"{lin.name} {variant}", act="gelu" if M % 2 else None)
+
+
 @pytest.mark.parametrize("M,N,K,yd", [(5, 136, 512, "f16"), (96, 264, 1280, "f32"), (257, 72, 256, "f16"),
                                       (33, 4096, 2560, "bf16")])
 def test_int4_f16_activations_and_outputs(lb, M, N, K, yd):
