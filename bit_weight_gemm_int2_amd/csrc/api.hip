@@ -26,6 +26,7 @@ hipError_t launch_gemm_int4(bool x_bf16, GemmArgs a, int num_cu, int variant, hi
 hipError_t launch_quantize(int fmt, const uint16_t* W, int64_t ldw, int64_t N, int64_t K, uint8_t* packed,
                            uint16_t* scales, int32_t* counter, hipStream_t st);
 int64_t int4_rows(int64_t M);
+size_t int4_workspace(int M, int N, int K, int num_cu, int variant);
 size_t small_workspace_bytes(int M, int N, int K, int num_cu, int variant, int count = 1);
 bool small_path(int M, int N, int K, int variant, int count = 1);
 }  // namespace lowbit
@@ -528,7 +529,9 @@ int32_t lowbit_gemm_grouped(int32_t count, int32_t format, const void* const* X,
 
 size_t lowbit_gemm_int4_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M < 1 || N < 1 || K < 128 || K % 128 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim) return 0;
-  return (size_t)(K / 128) * (size_t)lowbit::int4_rows(M) * sizeof(float);
+  int num_cu = 0;
+  if (current_device(&num_cu) != LOWBIT_OK) num_cu = 256;   // no gfx950 device: the MI355X's count
+  return lowbit::int4_workspace((int)M, (int)N, (int)K, num_cu, force_variant());
 }
 
 int32_t lowbit_gemm_int4(const void* X, int32_t x_dtype, int64_t M, int64_t K, int64_t ldx, const uint8_t* W_packed,

@@ -32,6 +32,7 @@ struct GemmArgs {
   float* ws;           // caller workspace: split-K partials (small M) or the 4-bit row sums
   const uint16_t* Z;   // fp16 zero points [N][K/128] (4-bit format only)
   int64_t ldr;         // row stride of the 4-bit row sums [K/128][ldr]
+  float* part;         // large-M kernel with a K split (gridDim.y > 1): FP32 partial planes [split][M][N]
 };
 
 // The operands of the problems of one grouped launch: same shapes, types and

@@ -141,6 +141,9 @@ __global__ __launch_bounds__(64 * WN) void gemm_large_kernel(GemmArgs a, int til
   }
   const int m0 = tm_i * BMT, n0 = tn_i * BN;
   const int G = a.K >> 7;
+  // K split (gridDim.y > 1, 4-bit launches only): this workgroup takes the
+  // groups [gb, ge) and leaves an FP32 partial tile; one split: all of K
+  const int gb = (int)(((int64_t)G * blockIdx.y) / gridDim.y), ge = (int)(((int64_t)G * (blockIdx.y + 1)) / gridDim.y);
   const int64_t wrow = I4 ? (a.K >> 1) : TERN ? (a.K >> 2) : (a.K >> 3);
   const float factor = I4 ? 1.0f : code_factor<TERN>();
   const int wcol0 = n0 + 64 * wave;                     // first column of this wave
@@ -217,17 +220,17 @@ __global__ __launch_bounds__(64 * WN) void gemm_large_kernel(GemmArgs a, int til
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
   float cref[2] = {1.0f, 1.0f};                 // reference scale of the accumulator
 
-  stage(0, 0);
-  if (NST == 3) stage(min(1, G - 1), 1);
+  stage(gb, 0);
+  if (NST == 3) stage(min(gb + 1, ge - 1), 1);
   int buf = 0;
-  for (int g = 0; g < G; ++g) {
+  for (int g = gb; g < ge; ++g) {
     // stage g complete (three stages: only this wave's stage g+1 loads may
     // be in flight), and every wave's part of it visible
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(NST == 3 ? stage_loads<FMT, WN, BMT>() : 0));
     __syncthreads();
     // past the end this copies the last group into a buffer nobody reads
-    if (NST == 3) stage(min(g + 2, G - 1), buf == 0 ? 2 : buf - 1);
-    else stage(min(g + 1, G - 1), buf ^ 1);
+    if (NST == 3) stage(min(g + 2, ge - 1), buf == 0 ? 2 : buf - 1);
+    else stage(min(g + 1, ge - 1), buf ^ 1);
     const uint8_t* xb = smem[buf];
     const uint8_t* wb = smem[buf] + X_BYTES + wave * (64 * CB);
     const uint8_t* sbuf = smem[buf] + X_BYTES + W_BYTES + wave * 256;
@@ -308,6 +311,25 @@ __global__ __launch_bounds__(64 * WN) void gemm_large_kernel(GemmArgs a, int til
   __builtin_amdgcn_s_waitcnt(0);                       // no DMA may still write LDS
 
   // ---- epilogue: final scale, bias, activation, one RNE cast, store ----
+  // (with a K split: the FP32 partial tile into plane blockIdx.y, nothing
+  // else; the reduce kernel adds the planes in split order and finishes)
+  if (gridDim.y > 1) {
+    float* P = a.part + (int64_t)blockIdx.y * a.M * a.N;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int n = n0 + 64 * wave + 32 * j + r32;
+      if (n >= a.N) continue;
+      const float c = cref[j];
+#pragma unroll
+      for (int i = 0; i < IB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int m = m0 + 32 * i + 8 * (r >> 2) + 4 * q + (r & 3);
+          if (m < a.M) P[(int64_t)m * a.N + n] = acc[i][j][r] * c;
+        }
+    }
+    return;
+  }
   const bool y16 = a.y_dtype != DT_F32;
   const bool vec = y16 && (a.ldy & 7) == 0 && ((uintptr_t)a.Y & 15) == 0;
   if (vec) {
@@ -935,6 +957,22 @@ __global__ void rowsum_kernel(const uint16_t* X, int64_t ldx, int M, int G, int6
   }
 }
 
+// The K-split 4-bit launch's second step: Y = act(sum over the splits, in
+// split order, of the FP32 partial planes + bias), one RNE cast. One thread
+// per output element (consecutive threads along N).
+__global__ void splitk_finish_kernel(const float* __restrict__ part, int S, int M, int N, const void* bias,
+                                     int bias_dtype, void* Y, int64_t ldy, int y_dtype, int act) {
+  const int64_t plane = (int64_t)M * N;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < plane;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int m = (int)(i / N), n = (int)(i - (int64_t)m * N);
+    float v = part[i];
+    for (int s = 1; s < S; ++s) v += part[s * plane + i];
+    const float b = bias ? load_bias(bias, bias_dtype, n) : 0.0f;
+    store_out(Y, ldy, y_dtype, m, n, finish(v, b, act));
+  }
+}
+
 // ===========================================================================
 // Host-side launch helpers
 // ===========================================================================
@@ -1238,6 +1276,44 @@ hipError_t launch_gemm(int fmt, bool x_bf16, GemmArgs a, int num_cu, int variant
 // Padded row count of the 4-bit row sums: every tile row the kernel reads.
 int64_t int4_rows(int64_t M) { return (M + 127) / 128 * 128 + 128; }
 
+struct Int4Plan {
+  bool small;   // 64 x 256 tiles
+  int splits;   // K split (1: none)
+};
+
+// Tile choice and K split of a 4-bit launch. 128-row tiles (128 x 512, or
+// 128 x 256 for N < 2048) unless they number fewer than the CUs; then 64 x
+// 256 tiles, two workgroups per CU, and while those still number no more
+// than the CUs allow, K is split (at most 4 ways, at least 4 groups
+// a split) so that splits x tiles stays within the CUs. variant 5 forces the
+// 128-row tiles, 6 the 64-row tiles without a split, 7 the 64-row tiles with
+// the largest split the groups allow (at most 4).
+Int4Plan int4_plan(int M, int N, int K, int num_cu, int variant) {
+  Int4Plan p{};
+  const int G = K >> 7;
+  const int64_t wide_tiles = (int64_t)((M + 127) / 128) * ((N + (N >= 2048 ? 511 : 255)) / (N >= 2048 ? 512 : 256));
+  p.small = variant == 6 || variant == 7 || (variant != 5 && wide_tiles < num_cu);
+  p.splits = 1;
+  if (p.small) {
+    const int64_t t = (int64_t)((M + 63) / 64) * ((N + 255) / 256);
+    if (variant == 7) {
+      p.splits = std::max(1, std::min(4, G / 4));
+    } else if (variant != 6) {
+      while (p.splits < 4 && t * (p.splits + 1) <= num_cu && G / (p.splits + 1) >= 4) ++p.splits;
+    }
+  }
+  return p;
+}
+
+// Workspace of a 4-bit launch: the row sums, then (K split) the partial
+// planes from the next 256-byte boundary.
+size_t int4_workspace(int M, int N, int K, int num_cu, int variant) {
+  const size_t sums = (size_t)(K / 128) * (size_t)int4_rows(M) * sizeof(float);
+  const Int4Plan p = int4_plan(M, N, K, num_cu, variant);
+  if (p.splits == 1) return sums;
+  return (sums + 255) / 256 * 256 + (size_t)p.splits * M * N * sizeof(float);
+}
+
 // 4-bit GEMM (any M): the row sums, then the large-M kernel with two stages
 // (a.ws: the row sums, a.ldr: int4_rows(M)). Tiles: 128 x 512 (eight waves,
 // one workgroup per CU) or 128 x 256 for narrow N; when those would leave
@@ -1252,13 +1328,23 @@ hipError_t launch_gemm_int4(bool x_bf16, GemmArgs a, int num_cu, int variant, hi
                      x_bf16 ? 1 : 0);
   const int tm = (a.M + large::BM - 1) / large::BM;
   const int xcd_cu = std::max(1, num_cu / 8);
-  const int64_t wide_tiles = (int64_t)tm * ((a.N + (a.N >= 2048 ? 511 : 255)) / (a.N >= 2048 ? 512 : 256));
-  const bool small = variant == 6 || (variant != 5 && wide_tiles < num_cu);
-  if (small) {
+  const Int4Plan plan = int4_plan(a.M, a.N, a.K, num_cu, variant);
+  if (plan.small) {
     const int tm4 = (a.M + 63) / 64, tn = (a.N + 255) / 256;
     const int xr = xcd_order(a.M, a.N, a.K, FMT_INT4, tm4, tn, 64, 256, 2 * xcd_cu);
-    if (x_bf16) hipLaunchKernelGGL((gemm_large_kernel<true, FMT_INT4, 4, 64, 2>), dim3(tm4 * tn), dim3(256), 0, st, a, tm4, tn, xr);
-    else hipLaunchKernelGGL((gemm_large_kernel<false, FMT_INT4, 4, 64, 2>), dim3(tm4 * tn), dim3(256), 0, st, a, tm4, tn, xr);
+    const dim3 grid(tm4 * tn, plan.splits);
+    if (plan.splits > 1) {
+      const size_t sums = (size_t)(a.K / 128) * (size_t)a.ldr * sizeof(float);
+      a.part = (float*)((uint8_t*)a.ws + (sums + 255) / 256 * 256);
+    }
+    if (x_bf16) hipLaunchKernelGGL((gemm_large_kernel<true, FMT_INT4, 4, 64, 2>), grid, dim3(256), 0, st, a, tm4, tn, xr);
+    else hipLaunchKernelGGL((gemm_large_kernel<false, FMT_INT4, 4, 64, 2>), grid, dim3(256), 0, st, a, tm4, tn, xr);
+    if (plan.splits > 1) {
+      const int64_t n = (int64_t)a.M * a.N;
+      const int64_t fb = std::min<int64_t>((n + 255) / 256, 16384);
+      hipLaunchKernelGGL(splitk_finish_kernel, dim3((unsigned)fb), dim3(256), 0, st, (const float*)a.part,
+                         plan.splits, a.M, a.N, a.bias, a.bias_dtype, a.Y, a.ldy, a.y_dtype, a.act);
+    }
   } else if (a.N >= 2048) {
     const int tn = (a.N + large::bn<8>() - 1) / large::bn<8>();
     const int xr = xcd_order(a.M, a.N, a.K, FMT_INT4, tm, tn, 128, 512, xcd_cu);

@@ -110,7 +110,8 @@ int32_t lowbit_init(void);
  * same shapes. name: "auto" or NULL (the automatic choice), "large" (the
  * large-M kernel at any M), "small" (the small-M kernels only), "large-wide"
  * / "large-pair" (one large-M tile configuration; for lowbit_gemm_int4 its
- * 128-row or its 64-row tiles), "small-split" (the
+ * 128-row or its 64-row tiles; "small-split" its 64-row tiles with the
+ * largest K split the groups allow), "small-split" (the
  * small-M column-tile kernel with its K split across workgroups). Results
  * keep the same accuracy contract under every variant, and the workspace
  * queries follow it. The initial value comes from the environment variable
@@ -299,8 +300,12 @@ int32_t lowbit_gemm_noalloc(int32_t format,
                             void* Y, int32_t y_dtype, int64_t ldy,
                             int32_t activation, void* stream);
 
-/* Workspace bytes lowbit_gemm_int4 needs: the per-group row sums of X,
- * K/128 x (M rounded up to 128, plus 128) FP32 values; 0 for a bad shape. */
+/* Workspace bytes lowbit_gemm_int4 needs (0 for a bad shape): the per-group
+ * row sums of X, K/128 x (M rounded up to 128, plus 128) FP32 values, and,
+ * when the launch splits K across workgroups (small grids: few tiles, long
+ * K), from the next 256-byte boundary, splits x M x N FP32 partial sums.
+ * Depends on (M, N, K) and the current device's CU count (256 is assumed
+ * when no gfx950 device is current). */
 size_t lowbit_gemm_int4_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /* The 4-bit group-quantised linear (any M), with a zero point per group:

@@ -128,6 +128,24 @@ def test_int4_each_tile_configuration(lb, variant, M, N, K):
     _assert_parity(Y, lin, f"{lin.name} {variant}", act="gelu" if M % 2 else None)
 
 
+@pytest.mark.parametrize("M,N,K,act", [(33, 300, 2048, None), (200, 520, 1280, "gelu"), (77, 1030, 4096, None),
+                                       (1, 256, 1024, "gelu")])
+def test_int4_k_split(lb, M, N, K, act):
+    """The K split of the 64-row configuration (forced with "small-split": the
+    largest split the groups allow, up to four): FP32 partial planes added in
+    split order by the finishing kernel, then bias, activation and the cast."""
+    banner(f"int4 gemm K split {M}x{N}x{K}")
+    lin = wl.make_int4_linear(f"i4s_{M}x{N}x{K}", M, N, K, "bf16", seed=5 * M + N + K, with_bias=True)
+    lb.force_variant("small-split")
+    try:
+        Y = _run(lb, lin, act=act)
+        Y2 = _run(lb, lin, act=act)
+    finally:
+        lb.force_variant(None)
+    assert np.array_equal(Y, Y2, equal_nan=True), "K-split result differs between two calls"
+    _assert_parity(Y, lin, f"{lin.name} split", act=act)
+
+
 @pytest.mark.parametrize("M,N,K,yd", [(5, 136, 512, "f16"), (96, 264, 1280, "f32"), (257, 72, 256, "f16"),
                                       (33, 4096, 2560, "bf16")])
 def test_int4_f16_activations_and_outputs(lb, M, N, K, yd):
