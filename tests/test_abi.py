@@ -73,7 +73,12 @@ def test_host_only_queries(L):
     assert L.lowbit_packed_bytes(b.INT4, 2560, 9728) == 2560 * 4864
     assert L.lowbit_packed_bytes(b.INT4, 4, 12) == -1          # K % 8
     # 4-bit row sums: one float per 128-group and padded row
-    assert L.lowbit_gemm_int4_workspace_bytes(512, 2560, 9728) == 76 * (512 + 128) * 4
+    assert L.lowbit_gemm_int4_workspace_bytes(4608, 9216, 3072) == 24 * (4608 + 128) * 4
+    # with a K split (no GPU here: a 256-CU device is assumed): 80 tiles of
+    # 64 x 256 at M = 512, N = 2560 take three splits; the planes follow the
+    # row sums from the next 256-byte boundary
+    sums = 76 * (512 + 128) * 4
+    assert L.lowbit_gemm_int4_workspace_bytes(512, 2560, 9728) == (sums + 255) // 256 * 256 + 3 * 512 * 2560 * 4
     assert L.lowbit_gemm_int4_workspace_bytes(1, 64, 256) == 2 * 256 * 4
     assert L.lowbit_gemm_int4_workspace_bytes(1, 64, 200) == 0
     assert L.lowbit_scale_count(3072, 9216, 128) == 3072 * 72
