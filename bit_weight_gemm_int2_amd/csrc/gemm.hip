@@ -489,6 +489,10 @@ __global__ __launch_bounds__(64 * WC * stream::kparts(WC, GS)) void gemm_stream_
   const int64_t wrow = TERN ? (a.K >> 2) : (a.K >> 3);
   const float factor = code_factor<TERN>();
 
+  // the bias of this lane's column, loaded first so that its latency hides
+  // behind the whole kernel (the oldest load: every wait below covers it)
+  const float bias_v = (a.bias && n < a.N) ? load_bias(a.bias, a.bias_dtype, n) : 0.0f;
+
   // (1) activations of the slice -> LDS: instruction t of this wave covers
   // rows 4j .. 4j+3 of group i (slot i of the tile). Issued from inline
   // assembly (scalar base + lane offset), so the compiler neither counts them
@@ -610,10 +614,9 @@ __global__ __launch_bounds__(64 * WC * stream::kparts(WC, GS)) void gemm_stream_
   const bool col_ok = n < a.N && lead;
   if (splits == 1) {
     if (col_ok) {
-      const float b = a.bias ? load_bias(a.bias, a.bias_dtype, n) : 0.0f;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (4 * q + e < a.M) store_out(a.Y, a.ldy, a.y_dtype, 4 * q + e, n, finish(acc[e], b, a.act));
+        if (4 * q + e < a.M) store_out(a.Y, a.ldy, a.y_dtype, 4 * q + e, n, finish(acc[e], bias_v, a.act));
     }
     return;
   }
@@ -710,10 +713,9 @@ __global__ __launch_bounds__(64 * WC * stream::kparts(WC, GS)) void gemm_stream_
   }
   if (stuck) __hip_atomic_fetch_add((int*)a.ws + stream::ERR_SLOT, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (col_ok) {
-    const float b = a.bias ? load_bias(a.bias, a.bias_dtype, n) : 0.0f;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      if (4 * q + e < a.M) store_out(a.Y, a.ldy, a.y_dtype, 4 * q + e, n, finish(sum[e], b, a.act));
+      if (4 * q + e < a.M) store_out(a.Y, a.ldy, a.y_dtype, 4 * q + e, n, finish(sum[e], bias_v, a.act));
   }
   if (tid == 0) __hip_atomic_store(ticket, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -778,6 +780,9 @@ __global__ __launch_bounds__(64 * (NCH == 1 ? thin::MAXWAVES : thin::MAXWAVES_CH
   const int64_t nc = min(n, a.N - 1);                       // columns past N: any valid column
   const uint8_t* wp = a.W + nc * wrow;
   uint8_t* xw = smem + (size_t)wave * NBUF * GW * 4096;
+  // the bias of this lane's column, loaded first (the oldest load, so every
+  // chunk wait below also covers it) and used only by wave 0 at the end
+  const float bias_v = (wave == 0 && a.bias && n < a.N) ? load_bias(a.bias, a.bias_dtype, n) : 0.0f;
   // only the row quads that hold rows < M are copied (rq of 1, 2 or 4);
   // fragment reads of rows past them read row r & (4 rq - 1) instead:
   // MFMA rows are independent and outputs of rows >= M are never stored
@@ -898,13 +903,28 @@ __global__ __launch_bounds__(64 * (NCH == 1 ? thin::MAXWAVES : thin::MAXWAVES_CH
   // sum of the waves' partials in wave order, epilogue; lane holds rows
   // 4q + e (e = 0..3) of column n
   if (wave == 0) {
-    f32x4 sum = red[0][lane];
-    for (int w2 = 1; w2 < nwav; ++w2) sum += red[w2][lane];
+    f32x4 sum;
+    if constexpr (NCH != 1) {
+      // several chunks (at most 8 waves): every partial read issued before
+      // the first add (one LDS round trip instead of one per wave), then
+      // added in wave order
+      f32x4 pw[thin::MAXWAVES_CHUNKED];
+#pragma unroll
+      for (int w2 = 0; w2 < thin::MAXWAVES_CHUNKED; ++w2)
+        pw[w2] = w2 < nwav ? red[w2][lane] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      sum = pw[0];
+#pragma unroll
+      for (int w2 = 1; w2 < thin::MAXWAVES_CHUNKED; ++w2)
+        if (w2 < nwav) sum += pw[w2];
+    } else {
+      // one chunk (up to 16 waves): in wave order, one read at a time
+      sum = red[0][lane];
+      for (int w2 = 1; w2 < nwav; ++w2) sum += red[w2][lane];
+    }
     if (n < a.N) {
-      const float b = a.bias ? load_bias(a.bias, a.bias_dtype, n) : 0.0f;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        if (4 * q + e < a.M) store_out(a.Y, a.ldy, a.y_dtype, 4 * q + e, n, finish(sum[e], b, a.act));
+        if (4 * q + e < a.M) store_out(a.Y, a.ldy, a.y_dtype, 4 * q + e, n, finish(sum[e], bias_v, a.act));
     }
   }
 }
