@@ -542,19 +542,26 @@ def bench_quantize(torch, lb, reps=10):
                            frac_hbm_peak=round(gbs3 / PEAK_HBM_GBS, 4)))
 
 
-def bench_int4(torch, lb, reps=50):
+def bench_int4(torch, lb, reps=50, fused=False):
     """The text encoder's 4-bit linears (lowbit_gemm_int4): the seven linears
     of one Qwen3-4B-shaped layer (q, k, v, o, gate, up, down) at 512 prompt
     tokens, bf16 activations, uniform 4-bit codes, FP16 scales and zero points
     per 128 (device draws, seed 16), each call with its row-sum pre-pass,
     back to back on one stream; beside torch.matmul (hipBLASLt) on dense bf16
-    weights of the same shapes."""
+    weights of the same shapes. fused: the linears that share an input run as
+    one, their weight rows concatenated (q|k|v 6144 x 2560, gate|up
+    19456 x 2560; four calls), on both sides."""
     import workloads as wl
     M = wl.TE_TOKENS
     gen = torch.Generator(device="cuda")
     gen.manual_seed(16)
     layer = []
-    for name, N, K in wl.text_encoder_shapes():
+    shapes = wl.text_encoder_shapes()
+    if fused:
+        d = {n: (N, K) for n, N, K in shapes}
+        shapes = [("qkv", d["q"][0] + d["k"][0] + d["v"][0], d["q"][1]), ("o",) + d["o"],
+                  ("gate_up", d["gate"][0] + d["up"][0], d["gate"][1]), ("down",) + d["down"]]
+    for name, N, K in shapes:
         q = torch.randint(0, 16, (N, K), generator=gen, device="cuda", dtype=torch.uint8)
         packed = lb.pack_int4(q)
         s = (torch.rand((N, K // 128), generator=gen, device="cuda") * 0.003 + 1e-4).half()
@@ -592,9 +599,12 @@ def bench_int4(torch, lb, reps=50):
     ms, dms = timed(lowbit), timed(dense)
     del layer
     torch.cuda.empty_cache()
-    return dict(M=M, linears=7, flop_per_layer=flop, ms_per_layer=round(ms, 4),
-                tflops=round(flop / (ms * 1e-3) / 1e12, 1), dense_bf16_ms=round(dms, 4),
-                dense_bf16_tflops=round(flop / (dms * 1e-3) / 1e12, 1))
+    out = dict(M=M, linears=len(shapes), flop_per_layer=flop, ms_per_layer=round(ms, 4),
+               tflops=round(flop / (ms * 1e-3) / 1e12, 1), dense_bf16_ms=round(dms, 4),
+               dense_bf16_tflops=round(flop / (dms * 1e-3) / 1e12, 1))
+    if not fused:
+        out["fused_same_input"] = bench_int4(torch, lb, reps, fused=True)
+    return out
 
 
 def traffic_probe(torch, lb):

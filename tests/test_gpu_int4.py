@@ -225,10 +225,11 @@ def test_int4_workspace_reuse(lb):
 
 # ------------------------------------------------- text-encoder layer shapes ---
 
-@pytest.mark.parametrize("name,N,K", wl.text_encoder_shapes())
+@pytest.mark.parametrize("name,N,K", wl.text_encoder_shapes() + [("qkv_fused", 6144, 2560), ("gate_up_fused", 19456, 2560)])
 def test_int4_text_encoder_layer(lb, name, N, K):
-    """The seven linears of one text-encoder layer at 512 prompt tokens; the
-    oracle checks 96 sampled rows (first and last included) of each."""
+    """The seven linears of one text-encoder layer at 512 prompt tokens, and
+    the two same-input fusions (q|k|v, gate|up rows concatenated); the oracle
+    checks 96 sampled rows (first and last included) of each."""
     banner(f"int4 text encoder {name} 512x{N}x{K}")
     lin = wl.make_int4_linear(f"te_{name}", wl.TE_TOKENS, N, K, "bf16", seed=N + K)
     Y = _run(lb, lin)
