@@ -1007,13 +1007,26 @@ __global__ void splitk_finish_kernel(const float* __restrict__ part, int S, int 
 // count beyond), two chunks in flight. With any_n the plan is also made for
 // wide N: the fallback when the column-tile plan cannot cover the shape
 // (more than MAXGS * MAXSPLIT groups of K, or too many column tiles).
-// A grouped launch of `count` problems counts the blocks of all of them.
+// A grouped launch of `count` problems counts the blocks of all of them; when
+// those fill one to two workgroups per CU and K has 16 groups or more, four
+// waves of two-group chunks (64 KiB of LDS) let two workgroups share a CU.
 struct ThinPlan { int gw, nch, waves, blocks; };
 
 static bool thin_plan(int M, int N, int K, int num_cu, ThinPlan* out, bool any_n = false, int count = 1) {
-  if (M > 16 || (!any_n && count * ((N + 15) / 16) >= num_cu)) return false;
+  if (M > 16) return false;
   const int G = K / 128;
   const int blocks = (N + 15) / 16;
+  // grouped launches whose column blocks fill one to two workgroups per CU
+  // (the image and text streams' 3072-column linears: 384 blocks): four
+  // waves of two-group chunks, 64 KiB of LDS, so two workgroups share a CU
+  // and every block runs in one round, with no K split across workgroups
+  const int64_t wgs = (int64_t)count * blocks;
+  if (!any_n && count > 1 && wgs >= num_cu && wgs <= 2 * (int64_t)num_cu && G >= 16) {
+    const int nch = (G + 7) / 8;                            // two-group chunks per wave, four waves
+    *out = ThinPlan{2, nch, (G + 2 * nch - 1) / (2 * nch), blocks};
+    return true;
+  }
+  if (!any_n && wgs >= num_cu) return false;
   constexpr size_t LDS = 160 * 1024, RED = 16 * 1024;      // LDS per workgroup, partials
   if ((G + 1) / 2 <= thin::MAXWAVES) {
     *out = ThinPlan{2, 1, (G + 1) / 2, blocks};
