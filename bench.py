@@ -35,10 +35,11 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_large_config3_traffic.json")
 
 
 def kernel_source_sha() -> str:
-    """Hash of the GEMM kernel source with comments and blank lines removed, so
-    that counter data stays attached to the code it was measured on."""
+    """Hash of the large-M kernel source (gemm_large.hip and common.h) with
+    comments and blank lines removed, so that counter data stays attached to
+    the code it was measured on."""
     h = hashlib.sha256()
-    for f in ("gemm.hip", "common.h"):
+    for f in ("gemm_large.hip", "common.h"):
         with open(os.path.join(ROOT, "bit_weight_gemm_int2_amd", "csrc", f)) as fh:
             for line in fh:
                 code = line.split("//", 1)[0].rstrip()

@@ -12,7 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "liblowbit.so")
-SOURCES = ["api.hip", "pack.hip", "gemm.hip", "quant.hip"]
+SOURCES = ["api.hip", "pack.hip", "gemm.hip", "gemm_large.hip", "quant.hip"]
 
 # Packed FP32 VALU instructions are disabled for all device code; plain
 # float code is scheduled as scalar v_fma_f32 / v_mul_f32 instead.

@@ -117,6 +117,9 @@ __device__ __forceinline__ void store_out(void* Y, int64_t ldy, int dtype, int m
   else ((float*)Y)[off] = v;
 }
 
+// s_waitcnt immediate for vmcnt(n), expcnt(7), lgkmcnt(0)
+constexpr int waitcnt_vm(int n) { return (n & 15) | (7 << 4) | ((n >> 4) << 14); }
+
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // Direct global -> LDS loads (global_load_lds_*) issued from inline assembly:
