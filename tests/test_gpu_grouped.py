@@ -57,8 +57,11 @@ def _check(lins, Ys, yd, gelu=False):
 
 @pytest.mark.parametrize("fmt", ["ternary", "binary"])
 @pytest.mark.parametrize("count,M,N,K", [
-    (2, 16, 3072, 3072),      # two 3072 x 3072 linears: 384 column blocks -> column tiles
-    (2, 16, 3072, 9216),      # long K: column tiles with the K split across workgroups
+    (2, 16, 3072, 3072),      # two 3072 x 3072 linears: 384 column blocks -> thin, two workgroups a CU
+    (2, 16, 3072, 9216),      # long K: the same thin pair, nine chunks a wave (runtime count)
+    (2, 1, 3072, 9216),       # the thin pair copying one row quad (M <= 4)
+    (2, 7, 3000, 2048),       # the thin pair with ragged N, two row quads and two chunks a wave
+    (3, 16, 1500, 4096),      # three problems, 282 blocks
     (2, 16, 9216, 3072),      # the double-stream fused QKV pair
     (6, 1, 3072, 3072),       # Q, K, V of both streams at M = 1
     (3, 5, 520, 6144),        # ragged N, K split inside the workgroup
