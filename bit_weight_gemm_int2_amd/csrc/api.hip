@@ -24,7 +24,7 @@ hipError_t launch_gemm(int fmt, bool x_bf16, GemmArgs a, int num_cu, int variant
 hipError_t launch_gelu(const void* in, void* out, int dtype, int64_t count, hipStream_t st);
 hipError_t launch_gemm_int4(bool x_bf16, GemmArgs a, int num_cu, int variant, hipStream_t st);
 hipError_t launch_quantize(int fmt, const uint16_t* W, int64_t ldw, int64_t N, int64_t K, uint8_t* packed,
-                           uint16_t* scales, int32_t* counter, hipStream_t st);
+                           uint16_t* scales, int32_t* counter, int variant, hipStream_t st);
 int64_t int4_rows(int64_t M);
 size_t int4_workspace(int M, int N, int K, int num_cu, int variant);
 size_t small_workspace_bytes(int M, int N, int K, int num_cu, int variant, int count = 1);
@@ -82,6 +82,8 @@ int parse_variant(const char* v) {
   if (!std::strcmp(v, "large-wide")) return 5;
   if (!std::strcmp(v, "large-pair")) return 6;
   if (!std::strcmp(v, "small-split")) return 7;
+  if (!std::strcmp(v, "quant-eighth")) return 8;
+  if (!std::strcmp(v, "quant-lane")) return 9;
   return -1;
 }
 
@@ -265,7 +267,7 @@ int32_t lowbit_quantize(int32_t format, const void* W, int64_t N, int64_t K, int
   int32_t st = current_device(nullptr);
   if (st) return st;
   hipError_t e = lowbit::launch_quantize(kernel_format(format), (const uint16_t*)W, ldw, N, K, packed,
-                                         (uint16_t*)scales, nonfinite_count, (hipStream_t)stream);
+                                         (uint16_t*)scales, nonfinite_count, force_variant(), (hipStream_t)stream);
   return e == hipSuccess ? LOWBIT_OK : LOWBIT_ERR_HIP;
 }
 

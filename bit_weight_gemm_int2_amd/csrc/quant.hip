@@ -37,16 +37,27 @@
 //  * that last rounding is done on the FP64 bit pattern (f64_to_f16_rne).
 //
 // Work layout: HBM-bound (2 bytes read, 0.25 or 0.125 written per weight).
-// An 8-lane eighth of a wave owns kQGroups consecutive groups of the
-// flattened [N][K/128] group array per pass; lane `sub` holds weights
-// 16 sub .. 16 sub + 15 of each group (two 16-byte loads per group, all
-// issued before any is used), which is exactly one INT2 word. Weights stay
-// in their 32-bit pairs: magnitudes, keep flags (one packed 16-bit subtract
-// per pair), signs and codes are formed two at a time with bit operations,
-// and non-finite weights are looked for with one packed maximum per pair
-// (the rare wave that has one takes a branch that counts and clears them).
-// Group sums are exchanged within the eighth (xor shuffles 1, 2, 4); binary
-// lanes pair their bits into a word with one more shuffle.
+// Two kernels:
+//  * quantize_kernel (both formats): an 8-lane eighth of a wave owns
+//    kQGroups consecutive groups of the flattened [N][K/128] group array per
+//    pass; lane `sub` holds weights 16 sub .. 16 sub + 15 of each group (two
+//    16-byte loads per group, all issued before any is used), which is
+//    exactly one INT2 word. Group sums are exchanged within the eighth (DPP
+//    moves); binary lanes pair their bits into a word with one more move.
+//  * quantize_lane_kernel (ternary, many groups): one lane owns a whole group
+//    (sixteen 16-byte loads), so the per-group work (threshold, division,
+//    rounding) is done once instead of in all eight lanes of an eighth, with
+//    no exchange at all. Its loads touch 64 cache lines per instruction and
+//    it needs many groups to fill the GPU: it gains only on launches of
+//    about half a gigabyte and more (from 2^21 groups); binary (already at
+//    the copy rate with eighths) and smaller ternary launches keep
+//    quantize_kernel.
+// In both, weights stay in their 32-bit pairs: magnitudes, keep flags (one
+// packed 16-bit subtract per pair), signs and codes are formed two at a time
+// with bit operations, and non-finite weights are looked for with one packed
+// maximum per pair (only a wave or lane that holds one takes the branch that
+// counts and clears them). In the lane kernel the kept weights are summed in
+// FP32 over each 16-weight word (exact, as above) and the word sums in FP64.
 #include "common.h"
 
 namespace lowbit {
@@ -245,12 +256,110 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
   }
 }
 
+// One 128-weight group per lane (ternary only; see the work layout above).
+constexpr int64_t kQuantLaneGroups = (int64_t)1 << 21;   // from this many groups on
+
+__global__ __launch_bounds__(256) void quantize_lane_kernel(const uint16_t* __restrict__ W, int64_t ldw, int64_t N,
+                                                            int G, uint32_t* __restrict__ packed,
+                                                            uint16_t* __restrict__ scales, int32_t* counter) {
+  const int64_t total = N * G;
+  const int64_t lanes = (int64_t)gridDim.x * blockDim.x;
+  int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  // (row, col) of group gid, advanced by the grid stride without a division per pass
+  const int64_t srow = lanes / G;
+  const int scol = (int)(lanes - srow * G);
+  int64_t row = gid / G;
+  int col = (int)(gid - row * G);
+  int bad = 0;
+  for (; gid < total; gid += lanes) {
+    const uint16_t* src = W + row * ldw + 128 * col;
+    uint32_t h[64];                                  // pair p: weights 2p (low half), 2p + 1
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const u32x4 v = *(const u32x4*)(src + 8 * i);
+      h[4 * i] = v[0];
+      h[4 * i + 1] = v[1];
+      h[4 * i + 2] = v[2];
+      h[4 * i + 3] = v[3];
+    }
+    uint32_t mx = 0;
+#pragma unroll
+    for (int p = 0; p < 64; ++p) mx = max16x2(mx, h[p] & 0x7FFF7FFFu);
+    if ((mx & 0xFFFFu) >= 0x7C00u || (mx >> 16) >= 0x7C00u) {
+      // count the non-finite weights and let them act as +0.0 (magnitude cleared)
+#pragma unroll
+      for (int p = 0; p < 64; ++p) {
+        const uint32_t nf = ((h[p] & 0x7FFF7FFFu) + 0x04000400u) & 0x80008000u;
+        bad += __builtin_popcount(nf);
+        h[p] &= ~(nf - (nf >> 15));
+      }
+    }
+    // exact FP64 sum of the magnitudes (four chains)
+    double part[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int p = 0; p < 64; ++p) {
+      part[p & 3] += (double)half_bits_to_float((uint16_t)(h[p] & 0x7FFFu));
+      part[p & 3] += (double)half_bits_to_float((uint16_t)((h[p] >> 16) & 0x7FFFu));
+    }
+    const double sum = (part[0] + part[1]) + (part[2] + part[3]);
+    const uint32_t thr = f16_floor_ratio(7.0 * sum);
+    const uint32_t thr2 = thr | (thr << 16);
+    double ksum = 0.0;
+    int cnt = 0;
+    u32x4 out[2];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {                    // INT2 word u: weights 16u .. 16u + 15
+      uint32_t word = 0;
+      float kept = 0.0f;                            // exact: 16 kept weights
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t hp = h[8 * u + j];
+        const uint32_t keep = sub16x2(thr2, hp & 0x7FFF7FFFu) & 0x80008000u;   // |w| > threshold
+        cnt += __builtin_popcount(keep);
+        // code 01 for +1, 11 for -1 at bits 2j (weight 2j) and 16 + 2j (weight 2j + 1)
+        word |= (keep >> (15 - 2 * j)) | ((hp & keep) >> (14 - 2 * j));
+        const uint32_t hk = hp & (keep - (keep >> 15));   // kept magnitudes, the others 0
+        kept += half_bits_to_float((uint16_t)(hk & 0xFFFFu));
+        kept += half_bits_to_float((uint16_t)(hk >> 16));
+      }
+      out[u >> 2][u & 3] = word;
+      ksum += (double)kept;
+    }
+    uint32_t* dst = packed + row * ((int64_t)G * 8) + 8 * col;
+    *(u32x4*)dst = out[0];
+    *(u32x4*)(dst + 4) = out[1];
+    scales[row * G + col] = (uint16_t)(cnt ? f64_to_f16_rne(ksum / (double)cnt) : 0u);
+    col += scol;
+    row += srow + (col >= G ? 1 : 0);
+    col -= col >= G ? G : 0;
+  }
+  if (counter) {
+    const unsigned long long m = __ballot(bad != 0);
+    if (m) {
+      int t = bad;
+      for (int off = 32; off > 0; off >>= 1) t += __shfl_xor(t, off);
+      if ((threadIdx.x & 63) == __builtin_ctzll(m)) atomicAdd(counter, t);
+    }
+  }
+}
+
 __global__ void quant_zero_kernel(int32_t* p) { *p = 0; }
 
+// variant: 8 forces quantize_kernel, 9 the lane kernel (ternary); otherwise
+// ternary launches of at least kQuantLaneGroups groups take the lane kernel.
 hipError_t launch_quantize(int fmt, const uint16_t* W, int64_t ldw, int64_t N, int64_t K, uint8_t* packed,
-                           uint16_t* scales, int32_t* counter, hipStream_t st) {
+                           uint16_t* scales, int32_t* counter, int variant, hipStream_t st) {
   if (counter) hipLaunchKernelGGL(quant_zero_kernel, dim3(1), dim3(1), 0, st, counter);
   const int G = (int)(K / 128);
+  if (fmt == FMT_TERNARY && (variant == 9 || (variant != 8 && N * G >= kQuantLaneGroups))) {
+    // at most 8192 workgroups (2^21 lanes, the same groups per pass as the
+    // eighths' grid below); the lanes walk the rest
+    int64_t blocks = (N * G + 255) / 256;
+    blocks = blocks < 1 ? 1 : (blocks > 8192 ? 8192 : blocks);
+    hipLaunchKernelGGL(quantize_lane_kernel, dim3((int)blocks), dim3(256), 0, st, W, ldw, N, G,
+                       (uint32_t*)packed, scales, counter);
+    return hipGetLastError();
+  }
   const int64_t eighths = (N * G + kQGroups - 1) / kQGroups;
   int64_t blocks = (eighths + 31) / 32;
   blocks = blocks < 1 ? 1 : (blocks > 32768 ? 32768 : blocks);

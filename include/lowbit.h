@@ -112,9 +112,12 @@ int32_t lowbit_init(void);
  * / "large-pair" (one large-M tile configuration; for lowbit_gemm_int4 its
  * 128-row or its 64-row tiles; "small-split" its 64-row tiles with the
  * largest K split the groups allow), "small-split" (the
- * small-M column-tile kernel with its K split across workgroups). Results
- * keep the same accuracy contract under every variant, and the workspace
- * queries follow it. The initial value comes from the environment variable
+ * small-M column-tile kernel with its K split across workgroups),
+ * "quant-eighth" / "quant-lane" (lowbit_quantize, ternary: eight lanes per
+ * group, or one lane per group; the automatic choice takes the second from
+ * 2^21 groups on). Results keep the same accuracy contract (bit-identical
+ * for lowbit_quantize) under every variant, and the workspace queries
+ * follow it. The initial value comes from the environment variable
  * LOWBIT_FORCE_VARIANT, read once. Returns LOWBIT_ERR_DTYPE for an unknown
  * name (the setting is then unchanged). Not for concurrent use with calls on
  * other threads that depend on the automatic choice. */

@@ -280,7 +280,8 @@ def test_variant_hook_names(L):
     """The test hook takes exactly the documented names; an unknown one is
     refused and leaves the setting alone."""
     import bit_weight_gemm_int2_amd as b
-    for name in (b"large", b"small", b"large-wide", b"large-pair", b"small-split", b"auto", None):
+    for name in (b"large", b"small", b"large-wide", b"large-pair", b"small-split", b"quant-eighth",
+                 b"quant-lane", b"auto", None):
         assert L.lowbit_debug_force_variant(name) == b.OK
     assert L.lowbit_debug_force_variant(b"bogus") == b.ERR_DTYPE
     b.force_variant(None)

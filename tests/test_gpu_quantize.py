@@ -127,9 +127,10 @@ def test_quantize_full_size_bit_exact(lb, fmt, N, K):
 
 
 def test_quantize_many_passes_sampled_rows(lb):
-    """More groups than one pass of the grid covers (about 2.1 million, ending
-    in a partial set of four), checked on sampled rows; the rule is row-local,
-    so a row's oracle result does not depend on the others."""
+    """More groups than one pass of the grid covers (2^21 for either ternary
+    kernel; this automatic launch takes the one-lane-per-group kernel),
+    checked on sampled rows; the rule is row-local, so a row's oracle result
+    does not depend on the others."""
     N, K = 21001, 12928                                  # 101 groups a row; N * 101 % 4 == 1
     print(f"[gpu] quantize ternary {N}x{K}, sampled rows", flush=True)
     g = wl.generator(70)
@@ -140,6 +141,45 @@ def test_quantize_many_passes_sampled_rows(lb):
     assert np.array_equal(packed[torch.from_numpy(rows).cuda()].cpu().numpy(), p_ref)
     assert np.array_equal(scales[torch.from_numpy(rows).cuda()].view(torch.int16).cpu().numpy().view(np.uint16),
                           s_ref)
+
+
+@pytest.fixture
+def quant_variant(lb, request):
+    lb.force_variant(request.param)
+    yield request.param
+    lb.force_variant(None)
+
+
+@pytest.mark.parametrize("quant_variant", ["quant-eighth", "quant-lane"], indirect=True)
+def test_each_ternary_kernel(lb, quant_variant):
+    """Both ternary kernels (eight lanes per group; one lane per group, which
+    the automatic choice takes from 2^21 groups on) on small, ragged, strided
+    and hand-built inputs, with the non-finite count and guard bands."""
+    print(f"[gpu] quantize ternary, {quant_variant}", flush=True)
+    for (N, K), seed in zip([(1, 128), (3, 256), (7, 384), (33, 1152), (130, 3072), (257, 640)], range(6)):
+        g = wl.generator(80 + seed)
+        _check(lb, wl.fp16_weights(g, N, K, outliers=0.01), "ternary")
+    full = wl.fp16_weights(wl.generator(86), 45, 640)
+    w = _dev16(full)[:, :512]
+    _check(lb, np.ascontiguousarray(full[:, :512]), "ternary", w_dev=w)
+    with open(os.path.join(os.path.dirname(__file__), "golden", "quantize_groups.json")) as f:
+        cases = json.load(f)["cases"]
+    w = np.array([[int(h, 16) for n, h in c["w"] for _ in range(n)] for c in cases], dtype=np.uint16)
+    p_ref, s_ref, bad_ref = _expect(w, "ternary")
+    N, K = w.shape
+    cnt = torch.empty(1, dtype=torch.int32, device="cuda")
+    pbuf = torch.full((N * K // 4 + 4096,), 0xA5, dtype=torch.uint8, device="cuda")
+    sbuf = torch.full((N * K // 128 + 2048,), -7, dtype=torch.int16, device="cuda")
+    wd = _dev16(w)
+    st = lb.lib().lowbit_quantize(lb.TERNARY, wd.data_ptr(), N, K, K, pbuf.data_ptr() + 2048,
+                                  sbuf.data_ptr() + 2048, cnt.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    assert st == lb.OK
+    assert int(cnt.item()) == bad_ref
+    ph, sh = pbuf.cpu().numpy(), sbuf.cpu().numpy()
+    assert (ph[:2048] == 0xA5).all() and (ph[2048 + N * K // 4:] == 0xA5).all()
+    assert np.array_equal(ph[2048:2048 + N * K // 4].reshape(N, K // 4), p_ref)
+    assert (sh[:1024] == -7).all() and (sh[1024 + N * K // 128:] == -7).all()
+    assert np.array_equal(sh[1024:1024 + N * K // 128].view(np.uint16).reshape(N, K // 128), s_ref)
 
 
 def test_quantized_weights_feed_the_gemm(lb):
