@@ -118,8 +118,8 @@ def workspace_bytes(fmt, M: int, N: int, K: int) -> int:
 
 def force_variant(name=None):
     """Test hook: force one kernel family ("large", "small", "large-wide",
-    "large-pair", "small-split"; for the quantiser "quant-eighth",
-    "quant-lane") for every later call of the process, or restore the
+    "large-pair", "small-split"; for the ternary quantiser "quant-eighth",
+    "quant-lane": eight or one lane per group) for every later call of the process, or restore the
     automatic choice with None / "auto"."""
     _check(lib().lowbit_debug_force_variant(None if name is None else name.encode()), "lowbit_debug_force_variant")
 

@@ -114,8 +114,7 @@ int32_t lowbit_init(void);
  * largest K split the groups allow), "small-split" (the
  * small-M column-tile kernel with its K split across workgroups),
  * "quant-eighth" / "quant-lane" (lowbit_quantize, ternary: eight lanes per
- * group, or one lane per group; the automatic choice takes the second from
- * 2^21 groups on). Results keep the same accuracy contract (bit-identical
+ * 128-weight group, or one lane per group, instead of the automatic two). Results keep the same accuracy contract (bit-identical
  * for lowbit_quantize) under every variant, and the workspace queries
  * follow it. The initial value comes from the environment variable
  * LOWBIT_FORCE_VARIANT, read once. Returns LOWBIT_ERR_DTYPE for an unknown

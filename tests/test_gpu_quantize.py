@@ -127,10 +127,9 @@ def test_quantize_full_size_bit_exact(lb, fmt, N, K):
 
 
 def test_quantize_many_passes_sampled_rows(lb):
-    """More groups than one pass of the grid covers (2^21 for either ternary
-    kernel; this automatic launch takes the one-lane-per-group kernel),
-    checked on sampled rows; the rule is row-local, so a row's oracle result
-    does not depend on the others."""
+    """More groups than one pass of the grid covers (2^21 groups), checked on
+    sampled rows; the rule is row-local, so a row's oracle result does not
+    depend on the others."""
     N, K = 21001, 12928                                  # 101 groups a row; N * 101 % 4 == 1
     print(f"[gpu] quantize ternary {N}x{K}, sampled rows", flush=True)
     g = wl.generator(70)
@@ -151,10 +150,10 @@ def quant_variant(lb, request):
 
 
 @pytest.mark.parametrize("quant_variant", ["quant-eighth", "quant-lane"], indirect=True)
-def test_each_ternary_kernel(lb, quant_variant):
-    """Both ternary kernels (eight lanes per group; one lane per group, which
-    the automatic choice takes from 2^21 groups on) on small, ragged, strided
-    and hand-built inputs, with the non-finite count and guard bands."""
+def test_each_ternary_team_size(lb, quant_variant):
+    """The ternary team sizes the automatic choice does not take (eight lanes
+    per group, one lane per group; it takes two) on small, ragged, strided and
+    hand-built inputs, with the non-finite count and guard bands."""
     print(f"[gpu] quantize ternary, {quant_variant}", flush=True)
     for (N, K), seed in zip([(1, 128), (3, 256), (7, 384), (33, 1152), (130, 3072), (257, 640)], range(6)):
         g = wl.generator(80 + seed)
