@@ -654,7 +654,7 @@ def traffic_summary(fetch_csv: str, write_csv: str) -> dict:
         "workload": "MLP pair of a 1024x1024 step: up 4608x9216x3072 (+GELU), down 4608x3072x9216, "
                     "bf16, ternary, group 128",
         "kernel_source_sha": kernel_source_sha(),
-        "kernel_source_sha_note": "sha256 of gemm.hip + common.h with // comments and blank lines removed "
+        "kernel_source_sha_note": "sha256 of gemm_large.hip + common.h with // comments and blank lines removed "
                                   "(bench.py kernel_source_sha)",
         "how": "hbm_bytes = (FETCH_SIZE_KiB * fetch_factor + WRITE_SIZE_KiB * write_factor) * 1024, mean over "
                "dispatches; factors = 262144 KiB / the counter value of a plain 256 MiB device copy",
