@@ -366,7 +366,10 @@ __global__ __launch_bounds__(64 * WN) void gemm_large_kernel(GemmArgs a, int til
       if (m < a.M) {
         uint16_t* dst = (uint16_t*)a.Y + (int64_t)m * a.ldy + n;
         if (n + 8 <= a.N) {
-          *(u32x4*)dst = v;
+          // non-temporal: the output is not read again by this launch, and
+          // keeping it out of L2 leaves room for the activation and code
+          // slices that the other workgroups of the XCD still read
+          __builtin_nontemporal_store(v, (u32x4*)dst);
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e)
