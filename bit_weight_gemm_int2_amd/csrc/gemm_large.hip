@@ -57,7 +57,9 @@ namespace lowbit {
 //    earlier), passes the barrier, and issues stage g+2 into the buffer of
 //    group g-1. Two stages: it waits for all its loads (stage g, issued one
 //    group earlier), passes the barrier and issues stage g+1 into the buffer
-//    of group g-1.
+//    of group g-1. The DMAs of that stage are spread over the group's first
+//    MFMA steps (all eight with three stages, four with two) rather than
+//    issued in one burst after the barrier.
 //  * Per MFMA step the wave reads the A fragments of the next step while
 //    the MFMAs of the current step run; the B operands of the step are
 //    unpacked from the group's codes (one 16- or 8-byte LDS read per column
@@ -182,31 +184,44 @@ __global__ __launch_bounds__(64 * WN) void gemm_large_kernel(GemmArgs a, int til
     woff[0] = woff[1] = (uint32_t)(min(wcol0 + lane, a.N - 1) * wrow);
   }
   soff = (uint32_t)(min(wcol0 + lane, a.N - 1) * (int64_t)G * 2);
-  auto stage = [&](int g, int buf) {
+  // DMA number d of stage g into LDS buffer `buf`, in this order: the
+  // activation rows (XR), the codes (one to four), the scales, and for the
+  // 4-bit format the zero points and the row sums
+  constexpr int NCODE = I4 ? 4 : TERN ? 2 : 1;
+  constexpr int ND = XR + NCODE + 1 + (I4 ? 2 : 0);
+  static_assert(ND == stage_loads<FMT, WN, BMT>(), "DMA count");
+  auto dma = [&](int g, int buf, int d) __attribute__((always_inline)) {
     uint8_t* base = smem[buf];
-    const uint8_t* xg = (const uint8_t*)a.X + ((int64_t)g << 8);
-#pragma unroll
-    for (int it = 0; it < XR; ++it)
-      dma_lds16(xg, xoff[it], lds_addr(base + (4 * XR * wave + 4 * it) * ROW_BYTES));
-    uint8_t* wb = base + X_BYTES + wave * (64 * CB);
-    const uint8_t* wg = a.W + g * (I4 ? 64 : TERN ? 32 : 16);
-    dma_lds16(wg, woff[0], lds_addr(wb));
-    if (TERN || I4) dma_lds16(wg, woff[1], lds_addr(wb + 1024));
-    if (I4) {
-      dma_lds16(wg, woff[2], lds_addr(wb + 2048));
-      dma_lds16(wg, woff[3], lds_addr(wb + 3072));
-    }
-    // scales: lane l -> 4-byte slot l (2-byte load, zero-extended)
-    dma_lds2((const uint8_t*)a.S + 2 * g, soff, lds_addr(base + X_BYTES + W_BYTES + wave * 256));
-    if (I4) {
-      // zero points likewise, then this wave's RW rows of the group's row
-      // sums (row-sum array padded past M, so every row read exists)
+    if (d < XR) {
+      const uint8_t* xg = (const uint8_t*)a.X + ((int64_t)g << 8);
+      dma_lds16(xg, xoff[d], lds_addr(base + (4 * XR * wave + 4 * d) * ROW_BYTES));
+    } else if (d < XR + NCODE) {
+      const uint8_t* wg = a.W + g * (I4 ? 64 : TERN ? 32 : 16);
+      dma_lds16(wg, woff[d - XR], lds_addr(base + X_BYTES + wave * (64 * CB) + 1024 * (d - XR)));
+    } else if (d == XR + NCODE) {
+      // scales: lane l -> 4-byte slot l (2-byte load, zero-extended)
+      dma_lds2((const uint8_t*)a.S + 2 * g, soff, lds_addr(base + X_BYTES + W_BYTES + wave * 256));
+    } else if (d == XR + NCODE + 1) {
+      // zero points likewise
       dma_lds2((const uint8_t*)a.Z + 2 * g, soff, lds_addr(base + X_BYTES + W_BYTES + BN * 4 + wave * 256));
+    } else {
+      // this wave's RW rows of the group's row sums (row-sum array padded
+      // past M, so every row read exists)
       const float* rg = a.ws + g * a.ldr + m0 + RW * wave;
       if (lane < RW / 4)
         dma_lds16(rg, 16 * lane, lds_addr(base + X_BYTES + W_BYTES + 2 * BN * 4 + 4 * RW * wave));
     }
   };
+  auto stage = [&](int g, int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int d = 0; d < ND; ++d) dma(g, buf, d);
+  };
+  // Inside the loop a stage's DMAs are spread over the first NP MFMA steps
+  // of the group (about one per step with three stages; over half the group
+  // with two, whose next wait comes one group later). Issued all at once
+  // right after the barrier, they would queue on the CU's memory pipeline
+  // and hold every wave's rescale and first MFMAs behind them.
+  constexpr int NP = NST == 3 ? 8 : 4;
 
   auto afrag = [&](const uint8_t* xb, int i, int s) -> u32x4 {
     const int r = 32 * i + r32;
@@ -229,9 +244,12 @@ __global__ __launch_bounds__(64 * WN) void gemm_large_kernel(GemmArgs a, int til
     // be in flight), and every wave's part of it visible
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(NST == 3 ? stage_loads<FMT, WN, BMT>() : 0));
     __syncthreads();
-    // past the end this copies the last group into a buffer nobody reads
-    if (NST == 3) stage(min(g + 2, ge - 1), buf == 0 ? 2 : buf - 1);
-    else stage(min(g + 1, ge - 1), buf ^ 1);
+    // the stage issued during this group (group g+2 with three stages, g+1
+    // with two) goes into the buffer of group g-1, which every wave has
+    // finished reading once past the barrier; past the end it copies the
+    // last group again into a buffer nobody reads
+    const int sg = NST == 3 ? min(g + 2, ge - 1) : min(g + 1, ge - 1);
+    const int sb = NST == 3 ? (buf == 0 ? 2 : buf - 1) : buf ^ 1;
     const uint8_t* xb = smem[buf];
     const uint8_t* wb = smem[buf] + X_BYTES + wave * (64 * CB);
     const uint8_t* sbuf = smem[buf] + X_BYTES + W_BYTES + wave * 256;
@@ -290,6 +308,10 @@ __global__ __launch_bounds__(64 * WN) void gemm_large_kernel(GemmArgs a, int til
 #pragma unroll
         for (int i = 0; i < IB; ++i) acc[i][j] = mfma32<BF16>(A[st & 1][i], bf, acc[i][j]);
       }
+      // this step's share of the next stage's DMAs
+#pragma unroll
+      for (int d = 0; d < ND; ++d)
+        if (d * NP / ND == st) dma(sg, sb, d);
     }
     if constexpr (I4) {
       // acc -= (128 + z) * (sum of the group's activations) per row, in the
