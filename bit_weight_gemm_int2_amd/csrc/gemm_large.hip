@@ -24,6 +24,7 @@
 // group as one 16-byte (ternary) or 8-byte (binary) load.
 #include <algorithm>
 #include <cmath>
+#include <type_traits>
 
 #include "common.h"
 
@@ -237,18 +238,24 @@ __global__ __launch_bounds__(64 * WN) void gemm_large_kernel(GemmArgs a, int til
   float cref[2] = {1.0f, 1.0f};                 // reference scale of the accumulator
 
   stage(gb, 0);
-  if (NST == 3) stage(min(gb + 1, ge - 1), 1);
+  if (NST == 3 && gb + 1 < ge) stage(gb + 1, 1);
   int buf = 0;
-  for (int g = gb; g < ge; ++g) {
-    // stage g complete (three stages: only this wave's stage g+1 loads may
-    // be in flight), and every wave's part of it visible
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(NST == 3 ? stage_loads<FMT, WN, BMT>() : 0));
+  // One group; MORE: the group NST - 1 ahead is staged during this one (the
+  // last NST - 1 groups run the same body without it, so no DMA is in flight
+  // after the last group that the epilogue would have to wait for).
+  auto run_group = [&](int g, auto more_tag) __attribute__((always_inline)) {
+    constexpr bool MORE = decltype(more_tag)::value;
+    // stage g complete (three stages: only this wave's stage g+1 loads, if
+    // there is a group g+1, may be in flight), and every wave's part of it
+    // visible
+    if (NST == 3 && g + 1 < ge) __builtin_amdgcn_s_waitcnt(waitcnt_vm(stage_loads<FMT, WN, BMT>()));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
     // the stage issued during this group (group g+2 with three stages, g+1
     // with two) goes into the buffer of group g-1, which every wave has
-    // finished reading once past the barrier; past the end it copies the
-    // last group again into a buffer nobody reads
-    const int sg = NST == 3 ? min(g + 2, ge - 1) : min(g + 1, ge - 1);
+    // finished reading once past the barrier (4-bit: past the end, a copy
+    // of the last group into a buffer nobody reads)
+    const int sg = min(NST == 3 ? g + 2 : g + 1, ge - 1);
     const int sb = NST == 3 ? (buf == 0 ? 2 : buf - 1) : buf ^ 1;
     const uint8_t* xb = smem[buf];
     const uint8_t* wb = smem[buf] + X_BYTES + wave * (64 * CB);
@@ -309,9 +316,11 @@ __global__ __launch_bounds__(64 * WN) void gemm_large_kernel(GemmArgs a, int til
         for (int i = 0; i < IB; ++i) acc[i][j] = mfma32<BF16>(A[st & 1][i], bf, acc[i][j]);
       }
       // this step's share of the next stage's DMAs
+      if constexpr (MORE) {
 #pragma unroll
-      for (int d = 0; d < ND; ++d)
-        if (d * NP / ND == st) dma(sg, sb, d);
+        for (int d = 0; d < ND; ++d)
+          if (d * NP / ND == st) dma(sg, sb, d);
+      }
     }
     if constexpr (I4) {
       // acc -= (128 + z) * (sum of the group's activations) per row, in the
@@ -330,6 +339,14 @@ __global__ __launch_bounds__(64 * WN) void gemm_large_kernel(GemmArgs a, int til
         }
     }
     buf = NST == 3 ? (buf == 2 ? 0 : buf + 1) : buf ^ 1;
+  };
+  int g = gb;
+  if constexpr (I4) {
+    // one loop body: a second copy makes the eight-wave 4-bit instance spill
+    for (; g < ge; ++g) run_group(g, std::true_type{});
+  } else {
+    for (; g + NST - 1 < ge; ++g) run_group(g, std::true_type{});
+    for (; g < ge; ++g) run_group(g, std::false_type{});
   }
   __builtin_amdgcn_s_waitcnt(0);                       // no DMA may still write LDS
 
