@@ -189,8 +189,10 @@ def test_small_and_large_kernels_agree_with_oracle(lb, force_variant, fmt, M, N,
 
 # shapes for both large-M tile configurations (128 x 512 / 128 x 256 wide
 # tiles, 96 x 256 pair tiles): ragged M and N, one or several tiles, odd
-# group counts
-_LARGE_SHAPES = [(100, 300, 1024), (257, 2100, 384), (96, 256, 128), (191, 4097, 640), (500, 1030, 1152)]
+# group counts, and one to three groups (fewer groups than the three-stage
+# pipeline is deep: no group is staged past the last)
+_LARGE_SHAPES = [(100, 300, 1024), (257, 2100, 384), (96, 256, 128), (191, 4097, 640), (500, 1030, 1152),
+                 (130, 2200, 256)]
 
 
 @pytest.mark.parametrize("fmt", ["ternary", "binary"])
